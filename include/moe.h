@@ -1,0 +1,198 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) single-GPU mixture-of-experts layer.
+ *
+ * The library computes one GPU's share of an MoE layer forward pass: router logits, top-k gating
+ * with softmax renormalisation, a device-side schedule that groups the routed rows by expert,
+ * a gather of the rows (fused with MXFP8 quantisation), SwiGLU expert FFNs as grouped GEMMs in
+ * BF16 or MXFP8, and a fixed-order weighted combine back to token order.
+ *
+ * The method is the Mixture-of-Kittens MoE layer ("Mixture-of-Kittens: Cursor's Open-Source MoE
+ * Training Megakernel for NVL72": TL;DR, flowchart, Key claims), restricted to what one GPU
+ * computes; the cross-GPU dispatch and combine are not part of this library.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless marked "host". All tensors are dense and row-major.
+ *     bfloat16 is passed as uint16_t bit patterns, E4M3 codes and E8M0 scales as uint8_t,
+ *     indices as int32_t.
+ *   - Notation: T source tokens, hidden h, expert width m, E router experts, top-k k, E_loc
+ *     experts held by this GPU, R = T*k routed rows, assignment a = t*k + j (token t, slot j).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call only enqueues
+ *     work on it: no host synchronisation, no allocation, no state kept between calls. Shapes
+ *     alone size every launch; the device-side expert counts are never read by the host.
+ *   - Ownership: the caller owns every buffer, including workspaces (sized by the *_bytes
+ *     queries) and prepared weights. Buffers must not overlap unless stated.
+ *   - Alignment: every pointer must be 256-byte aligned (torch allocations are).
+ *   - Errors: arguments are checked on the host before anything is enqueued. MOE_EINVAL means a
+ *     null required pointer, a misaligned pointer or an inconsistent shape, and nothing was
+ *     enqueued. MOE_EUNSUPPORTED means a valid shape the kernels do not cover (see each call).
+ *     MOE_EHIP means a launch failed (hipGetLastError). No C++ exception crosses the ABI.
+ *   - Determinism: there are no floating-point atomics and no split reductions; every sum has a
+ *     fixed order, so identical inputs give bitwise identical outputs (the page's "bitwise
+ *     deterministic" property, TL;DR and Key claims).
+ *   - Thread safety: calls on different streams with different buffers may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EHIP = 3
+} moe_status;
+
+/* Expert GEMM precision. MOE_MXFP8: E4M3 elements with one E8M0 scale per 32 consecutive elements
+ * along each GEMM's reduction axis (OCP Microscaling v1.0); the page's Key claims make MXFP8 the
+ * default with activation quantisation fused into dispatch, the grouped GEMMs and the SwiGLU. */
+typedef enum { MOE_BF16 = 0, MOE_MXFP8 = 1 } moe_dtype;
+
+typedef struct {
+  int32_t T;        /* source tokens, >= 1 */
+  int32_t h;        /* hidden size, multiple of 64 (MXFP8: of 256) */
+  int32_t m;        /* expert intermediate width, multiple of 32 (MXFP8: of 256) */
+  int32_t E;        /* router experts, >= k (only the router uses it) */
+  int32_t k;        /* top-k, 1 <= k <= min(E, 16) */
+  int32_t E_loc;    /* experts held by this GPU, 1 .. 1024 (router use: E_loc == E) */
+  int32_t m_shared; /* width of a BF16 shared SwiGLU expert over the T tokens, 0 = none */
+} moe_shape;
+
+const char* moe_status_string(moe_status s);
+int moe_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Weight preparation (offline, not part of a forward pass).
+ *
+ * w_gate, w_up: [E_loc][h][m] bf16 (y = x W convention); w_down: [E_loc][m][h] bf16.
+ * `prepared` receives moe_prepared_weight_bytes() bytes in the layout the grouped GEMMs read:
+ *   MOE_BF16 : W1[e][2m][h] bf16 (row n = output column n of GEMM-1; gate and up columns
+ *              interleaved in blocks of 32: rows 64c..64c+31 are gate columns 32c..32c+31,
+ *              rows 64c+32..64c+63 the up columns of the same range), then W2[e][h][m] bf16
+ *              (W_down transposed).
+ *   MOE_MXFP8: the same two matrices as E4M3 codes, each followed by its E8M0 scales
+ *              ([e][2m][h/32] and [e][h][m/32]): blocks of 32 run along h for W1 and along m for
+ *              W2, i.e. along each GEMM's reduction axis.
+ * The shared expert is prepared with the same call, shape.E_loc = 1, shape.m = m_shared, MOE_BF16.
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_prepared_weight_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_prepare_weights(const moe_shape* s, moe_dtype dt, const uint16_t* w_gate,
+                               const uint16_t* w_up, const uint16_t* w_down, void* prepared,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_route: router logits, top-k, renormalised softmax weights ("token routing" of the page's
+ * companion news digest, Merged summary; the workloads define softmax over logits, top-k,
+ * renormalise).
+ *
+ * x [T][h] bf16; w_router [E][h] bf16 (row e = expert e); bias [E] float or NULL.
+ * logits [T][E] float (output): l[t,e] = sum_i x[t,i] w_router[e,i] + bias[e], summed in float32
+ *   in the fixed order i = 0 .. h-1 starting from +0.0 (one rounding per step), then + bias.
+ * topk_idx [T][k] int32 (output): the k largest logits per token, logit descending, lower expert
+ *   index first on ties, -0.0 equal to +0.0; slot j holds the j-th ranked expert.
+ * topk_w [T][k] float (output): exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected.
+ * Requires E_loc == E. Unsupported: E > 1024 or k > 16.
+ * ------------------------------------------------------------------------------------------- */
+moe_status moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                     const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_permute: the device-side schedule and the gather (the page's flowchart: a device-side
+ * schedule kernel with no CPU synchronisation; Key claims: dynamic per-expert counts absorbed by
+ * a fixed-size buffer, no host synchronisation; quantisation fused into dispatch).
+ *
+ * assign [T*k] int32: local expert of assignment a (0 <= assign[a] < E_loc; e.g. topk_idx).
+ * x [T][h] bf16.
+ * Outputs: counts [E_loc], offsets [E_loc+1] (exclusive scan), perm [R] (routed row r holds
+ *   assignment perm[r]; rows of expert e are offsets[e] .. offsets[e+1]-1 with assignments
+ *   ascending), inv [R] (inv[perm[r]] == r), and the routed rows (capacity R, nothing dropped):
+ *   MOE_BF16 : rows [R][h] bf16, rows[r] = x[perm[r] / k]; row_scales unused (may be NULL).
+ *   MOE_MXFP8: rows [R][h] E4M3 codes and row_scales [R][h/32] E8M0 of x[perm[r] / k], quantised
+ *              per 32 along h: s = floor(log2 amax) - 8 clamped to [-127, 127] (s = -127 for an
+ *              all-zero block), code = E4M3(v / 2^s) with round-to-nearest-even, saturation at
+ *              448, sign of zero kept; scale byte s + 127. Each token is quantised once.
+ * ws: moe_permute_workspace_bytes() bytes of scratch.
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_permute_workspace_bytes(const moe_shape* s);
+moe_status moe_permute(const moe_shape* s, moe_dtype dt, const int32_t* assign,
+                       const uint16_t* x, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* rows, uint8_t* row_scales, void* ws, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_expert_ffn: the SwiGLU experts as grouped GEMMs (Key claims: expert grouped GEMMs, MXFP8,
+ * fused SwiGLU, fused quantisation).
+ *
+ * For each local expert e and each routed row r in offsets[e] .. offsets[e+1]-1:
+ *   G = rows[r] W_gate[e], U = rows[r] W_up[e] (float32 accumulation), H = silu(G) * U,
+ *   out_rows[r] = H W_down[e] rounded to bf16.
+ *   MOE_BF16 : H is rounded to bf16 before the second GEMM.
+ *   MOE_MXFP8: rows/row_scales as written by moe_permute; H is MX-quantised per 32 along m from
+ *              its float32 value inside the first GEMM's epilogue.
+ * rows: R = T*k rows (for the shared expert: T rows with shape.k = 1, E_loc = 1, offsets {0, T}).
+ * offsets [E_loc+1] device int32 (from moe_permute); prepared from moe_prepare_weights.
+ * ws: moe_expert_ffn_workspace_bytes() bytes (holds the tile table and H).
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_expert_ffn_workspace_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_expert_ffn(const moe_shape* s, moe_dtype dt, const void* rows,
+                          const uint8_t* row_scales, const int32_t* offsets, const void* prepared,
+                          uint16_t* out_rows, void* ws, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_combine: y[t] = S[t] + sum_{j = 0 .. k-1, ascending} w[t*k+j] * out_rows[inv[t*k+j]],
+ * accumulated in float32 starting from S[t] (or +0.0) and rounded to bf16 once (the page's fixed
+ * floating-point order, TL;DR and Key claims). Gather form, no atomics.
+ * out_rows [R][h] bf16; inv [R]; topk_w [R] float; shared_out [T][h] bf16 or NULL; y [T][h] bf16.
+ * ------------------------------------------------------------------------------------------- */
+moe_status moe_combine(const moe_shape* s, const uint16_t* out_rows, const int32_t* inv,
+                       const float* topk_w, const uint16_t* shared_out, uint16_t* y,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_forward: the whole layer on one stream, no host synchronisation:
+ *   route (if w_router != NULL) -> permute -> expert FFN -> [shared expert] -> combine.
+ * x [T][h] bf16.
+ * Router use: w_router [E][h], bias [E] or NULL; assign/assign_w must be NULL; E_loc == E.
+ * Expert-share use: w_router == NULL; assign [T*k] local expert ids and assign_w [T*k] gate
+ *   weights given by the caller (one expert-parallel rank's share).
+ * prepared: E_loc experts from moe_prepare_weights(dt); shared_prepared: BF16 shared expert
+ *   (shape.m_shared > 0) or NULL. y [T][h] bf16 output.
+ * ws: moe_forward_workspace_bytes() bytes. The intermediates stay in it; moe_forward_views()
+ *   gives their addresses.
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_forward_workspace_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                       const uint16_t* w_router, const float* bias, const int32_t* assign,
+                       const float* assign_w, const void* prepared, const void* shared_prepared,
+                       uint16_t* y, void* ws, void* stream);
+
+/* Addresses of the intermediates moe_forward leaves in `ws` (device pointers into ws; NULL when a
+ * buffer does not exist for this shape). Host-only arithmetic, nothing is enqueued. */
+typedef struct {
+  float* logits;       /* [T][E]      router use only */
+  int32_t* topk_idx;   /* [T][k]      router use only */
+  float* topk_w;       /* [T][k]      router use only */
+  int32_t* counts;     /* [E_loc] */
+  int32_t* offsets;    /* [E_loc+1] */
+  int32_t* perm;       /* [R] */
+  int32_t* inv;        /* [R] */
+  void* rows;          /* [R][h] bf16 or E4M3 */
+  uint8_t* row_scales; /* [R][h/32]   MXFP8 only */
+  uint16_t* out_rows;  /* [R][h] bf16 */
+  uint16_t* shared_out;/* [T][h] bf16 shared expert output, if any */
+} moe_forward_views_t;
+moe_status moe_forward_views(const moe_shape* s, moe_dtype dt, void* ws,
+                             moe_forward_views_t* views /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

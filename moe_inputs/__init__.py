@@ -256,3 +256,49 @@ def shared_weights(wl: Workload, seed: int = 0):
         _normal_bf16(seed, "shared/w_up", wl.h, ms, 1.0 / wl.h),
         _normal_bf16(seed, "shared/w_down", ms, wl.h, 1.0 / ms),
     )
+
+
+# ------------------------------------------------------------------------------------------------
+# Device-side generation of expert weights for full-size runs (GPU harness and bench). Each expert
+# has its own torch CUDA generator seeded from (seed, name, expert); values are N(0, 1/fan_in)
+# drawn in float32 and rounded to bfloat16 by torch. The oracle reads the same tensors back.
+# ------------------------------------------------------------------------------------------------
+
+
+def _torch_seed(seed: int, name: str, e: int) -> int:
+    ss = np.random.SeedSequence((seed, _tag(name), e, 0x7E57))
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64((1 << 63) - 1))
+
+
+def torch_expert_weights(wl: Workload, device, seed: int = 0):
+    """Stacked W_gate, W_up [E_loc, h, m] and W_down [E_loc, m, h] as torch bfloat16 on `device`."""
+    import torch
+
+    out = []
+    for name, (a, b), var in (("tw_gate", (wl.h, wl.m), 1.0 / wl.h),
+                              ("tw_up", (wl.h, wl.m), 1.0 / wl.h),
+                              ("tw_down", (wl.m, wl.h), 1.0 / wl.m)):
+        t = torch.empty((wl.E_loc, a, b), dtype=torch.bfloat16, device=device)
+        g = torch.Generator(device=device)
+        for e in range(wl.E_loc):
+            g.manual_seed(_torch_seed(seed, name, e))
+            t[e].copy_(torch.randn((a, b), generator=g, device=device, dtype=torch.float32)
+                       .mul_(float(np.sqrt(var))))
+        out.append(t)
+    return tuple(out)
+
+
+def torch_shared_weights(wl: Workload, device, seed: int = 0):
+    """The shared expert's W_gate, W_up [h, m_s], W_down [m_s, h] as torch bfloat16."""
+    import torch
+
+    ms = wl.m_shared
+    out = []
+    for name, (a, b), var in (("tshared/w_gate", (wl.h, ms), 1.0 / wl.h),
+                              ("tshared/w_up", (wl.h, ms), 1.0 / wl.h),
+                              ("tshared/w_down", (ms, wl.h), 1.0 / ms)):
+        g = torch.Generator(device=device)
+        g.manual_seed(_torch_seed(seed, name, 0))
+        out.append(torch.randn((a, b), generator=g, device=device, dtype=torch.float32)
+                   .mul_(float(np.sqrt(var))).to(torch.bfloat16))
+    return tuple(out)

@@ -1,0 +1,224 @@
+"""MI355X (gfx950) single-GPU mixture-of-experts layer: Python binding of libmoe_mi355x.so.
+
+Every function here marshals torch tensors (device memory) and the current torch stream into the
+C ABI of include/moe.h and allocates outputs the caller did not pass; all computation happens in
+the library's HIP kernels. The names follow the C entry points.
+
+Tensors: bfloat16 tensors for bf16 data, torch.uint8 for E4M3 codes / E8M0 scales / prepared
+weights / workspaces, int32 for indices, float32 for logits and gate weights. All must be
+contiguous CUDA tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import (MOE_BF16, MOE_MXFP8, MoeError, MoeForwardViews, MoeShape, check, load)
+
+__all__ = [
+    "MOE_BF16", "MOE_MXFP8", "MoeError", "make_shape", "dtype_code",
+    "moe_prepared_weight_bytes", "moe_prepare_weights", "moe_route", "moe_permute_workspace_bytes",
+    "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+    "moe_forward_workspace_bytes", "moe_forward", "moe_forward_views",
+]
+
+
+def make_shape(T: int, h: int, m: int, E: int, k: int, E_loc: Optional[int] = None,
+               m_shared: int = 0) -> MoeShape:
+    return MoeShape(T, h, m, E, k, E if E_loc is None else E_loc, m_shared)
+
+
+def dtype_code(dtype) -> int:
+    if dtype in (MOE_BF16, "bf16"):
+        return MOE_BF16
+    if dtype in (MOE_MXFP8, "mxfp8"):
+        return MOE_MXFP8
+    raise ValueError(f"unknown expert dtype {dtype!r}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _dev(ref: torch.Tensor):
+    return ref.device
+
+
+def moe_prepared_weight_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_prepared_weight_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_prepare_weights(shape: MoeShape, dtype, w_gate, w_up, w_down, prepared=None, stream=None):
+    dt = dtype_code(dtype)
+    n = moe_prepared_weight_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_prepared_weight_bytes", 1, "shape rejected")
+    if prepared is None:
+        prepared = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
+    e, h, m = shape.E_loc, shape.h, shape.m
+    check("moe_prepare_weights", load().moe_prepare_weights(
+        ctypes.byref(shape), dt,
+        _ptr(w_gate, "w_gate", torch.bfloat16, e * h * m),
+        _ptr(w_up, "w_up", torch.bfloat16, e * h * m),
+        _ptr(w_down, "w_down", torch.bfloat16, e * m * h),
+        _ptr(prepared, "prepared", torch.uint8, n), _stream(stream)))
+    return prepared
+
+
+def moe_route(shape: MoeShape, x, w_router, bias=None, logits=None, topk_idx=None, topk_w=None,
+              stream=None):
+    T, E, k = shape.T, shape.E, shape.k
+    dev = _dev(x)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits
+    topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    check("moe_route", load().moe_route(
+        ctypes.byref(shape), _ptr(x, "x", torch.bfloat16, T * shape.h),
+        _ptr(w_router, "w_router", torch.bfloat16, E * shape.h),
+        _ptr(bias, "bias", torch.float32, E),
+        _ptr(logits, "logits", torch.float32, T * E),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _stream(stream)))
+    return logits, topk_idx, topk_w
+
+
+def moe_permute_workspace_bytes(shape: MoeShape) -> int:
+    return load().moe_permute_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_permute(shape: MoeShape, dtype, assign, x, out: Optional[dict] = None, ws=None,
+                stream=None) -> dict:
+    dt = dtype_code(dtype)
+    T, h, k, E_loc = shape.T, shape.h, shape.k, shape.E_loc
+    R = T * k
+    dev = _dev(x)
+    o = dict(out or {})
+    o.setdefault("counts", torch.empty(E_loc, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(E_loc + 1, dtype=torch.int32, device=dev))
+    o.setdefault("perm", torch.empty(R, dtype=torch.int32, device=dev))
+    o.setdefault("inv", torch.empty(R, dtype=torch.int32, device=dev))
+    if dt == MOE_MXFP8:
+        o.setdefault("rows", torch.empty(R, h, dtype=torch.uint8, device=dev))
+        o.setdefault("row_scales", torch.empty(R, h // 32, dtype=torch.uint8, device=dev))
+    else:
+        o.setdefault("rows", torch.empty(R, h, dtype=torch.bfloat16, device=dev))
+        o.setdefault("row_scales", None)
+    nws = moe_permute_workspace_bytes(shape)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if ws is None else ws
+    check("moe_permute", load().moe_permute(
+        ctypes.byref(shape), dt, _ptr(assign, "assign", torch.int32, R),
+        _ptr(x, "x", torch.bfloat16, T * h), _ptr(o["counts"], "counts", torch.int32, E_loc),
+        _ptr(o["offsets"], "offsets", torch.int32, E_loc + 1),
+        _ptr(o["perm"], "perm", torch.int32, R), _ptr(o["inv"], "inv", torch.int32, R),
+        _ptr(o["rows"], "rows"), _ptr(o["row_scales"], "row_scales"), _ptr(ws, "ws"),
+        _stream(stream)))
+    return o
+
+
+def moe_expert_ffn_workspace_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_expert_ffn_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_expert_ffn(shape: MoeShape, dtype, rows, row_scales, offsets, prepared, out_rows=None,
+                   ws=None, stream=None):
+    dt = dtype_code(dtype)
+    R = shape.T * shape.k
+    dev = _dev(rows)
+    out_rows = torch.empty(R, shape.h, dtype=torch.bfloat16, device=dev) if out_rows is None \
+        else out_rows
+    n = moe_expert_ffn_workspace_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_expert_ffn_workspace_bytes", 1, "shape rejected")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    check("moe_expert_ffn", load().moe_expert_ffn(
+        ctypes.byref(shape), dt, _ptr(rows, "rows"), _ptr(row_scales, "row_scales"),
+        _ptr(offsets, "offsets", torch.int32, shape.E_loc + 1), _ptr(prepared, "prepared"),
+        _ptr(out_rows, "out_rows", torch.bfloat16, R * shape.h), _ptr(ws, "ws"),
+        _stream(stream)))
+    return out_rows
+
+
+def moe_combine(shape: MoeShape, out_rows, inv, topk_w, shared_out=None, y=None, stream=None):
+    T, h, k = shape.T, shape.h, shape.k
+    y = torch.empty(T, h, dtype=torch.bfloat16, device=_dev(out_rows)) if y is None else y
+    check("moe_combine", load().moe_combine(
+        ctypes.byref(shape), _ptr(out_rows, "out_rows", torch.bfloat16),
+        _ptr(inv, "inv", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(shared_out, "shared_out", torch.bfloat16, T * h),
+        _ptr(y, "y", torch.bfloat16, T * h), _stream(stream)))
+    return y
+
+
+def moe_forward_workspace_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_forward_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, assign=None,
+                assign_w=None, shared_prepared=None, y=None, ws=None, stream=None):
+    """The whole layer. Returns (y, ws); moe_forward_views(shape, dtype, ws) exposes the
+    intermediates left in ws."""
+    dt = dtype_code(dtype)
+    T, h, k = shape.T, shape.h, shape.k
+    dev = _dev(x)
+    y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
+    n = moe_forward_workspace_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_forward_workspace_bytes", 1, "shape rejected")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    check("moe_forward", load().moe_forward(
+        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h), _ptr(w_router, "w_router"),
+        _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
+        _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
+        _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
+        _ptr(ws, "ws"), _stream(stream)))
+    return y, ws
+
+
+def moe_forward_views(shape: MoeShape, dtype, ws) -> dict:
+    """Tensors viewing the intermediates moe_forward leaves in ws (None where absent)."""
+    dt = dtype_code(dtype)
+    v = MoeForwardViews()
+    check("moe_forward_views", load().moe_forward_views(ctypes.byref(shape), dt,
+                                                         ctypes.c_void_p(ws.data_ptr()),
+                                                         ctypes.byref(v)))
+    T, h, k, E, E_loc = shape.T, shape.h, shape.k, shape.E, shape.E_loc
+    R = T * k
+    base = ws.data_ptr()
+
+    def view(ptr, nbytes, dtype_, shp):
+        if not ptr:
+            return None
+        off = ptr - base
+        return ws[off:off + nbytes].view(dtype_).view(*shp)
+
+    mx = dt == MOE_MXFP8
+    return {
+        "logits": view(v.logits, T * E * 4, torch.float32, (T, E)),
+        "topk_idx": view(v.topk_idx, R * 4, torch.int32, (T, k)),
+        "topk_w": view(v.topk_w, R * 4, torch.float32, (T, k)),
+        "counts": view(v.counts, E_loc * 4, torch.int32, (E_loc,)),
+        "offsets": view(v.offsets, (E_loc + 1) * 4, torch.int32, (E_loc + 1,)),
+        "perm": view(v.perm, R * 4, torch.int32, (R,)),
+        "inv": view(v.inv, R * 4, torch.int32, (R,)),
+        "rows": view(v.rows, R * h * (1 if mx else 2), torch.uint8 if mx else torch.bfloat16,
+                     (R, h)),
+        "row_scales": view(v.row_scales, R * (h // 32), torch.uint8, (R, h // 32)),
+        "out_rows": view(v.out_rows, R * h * 2, torch.bfloat16, (R, h)),
+        "shared_out": view(v.shared_out, T * h * 2, torch.bfloat16, (T, h)),
+    }

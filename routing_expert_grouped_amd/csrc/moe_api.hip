@@ -1,0 +1,286 @@
+// C-ABI front end: argument checks, workspace layout and the launch sequence of each entry point.
+// Nothing here allocates or synchronises; every call only enqueues kernels on the caller's stream.
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxK = 16;
+constexpr int kMaxExperts = 1024;
+constexpr uintptr_t kPtrAlign = 16;
+
+bool ok_ptr(const void* p) { return p != nullptr && ((uintptr_t)p % kPtrAlign) == 0; }
+bool ok_opt(const void* p) { return p == nullptr || ((uintptr_t)p % kPtrAlign) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Shape rules of the expert path. EINVAL: inconsistent; EUNSUPPORTED: valid but not tiled.
+moe_status check_expert_shape(const moe_shape* s, moe_dtype dt) {
+  if (!s) return MOE_EINVAL;
+  if (s->T < 1 || s->h < 1 || s->m < 1 || s->k < 1 || s->E_loc < 1 || s->m_shared < 0)
+    return MOE_EINVAL;
+  if (dt != MOE_BF16 && dt != MOE_MXFP8) return MOE_EINVAL;
+  if (dt == MOE_MXFP8 && (s->h % kMxBlock || s->m % kMxBlock)) return MOE_EINVAL;
+  if (s->k > kMaxK || s->E_loc > kMaxExperts) return MOE_EUNSUPPORTED;
+  if ((long long)s->T * s->k > (1ll << 30)) return MOE_EUNSUPPORTED;
+  if (s->h % 128) return MOE_EUNSUPPORTED;
+  if (s->m % 64) return MOE_EUNSUPPORTED;
+  if (dt == MOE_MXFP8 && (s->h % 256 || s->m % 256)) return MOE_EUNSUPPORTED;
+  if (s->m_shared && s->m_shared % 64) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_router_shape(const moe_shape* s) {
+  if (!s) return MOE_EINVAL;
+  if (s->T < 1 || s->h < 1 || s->k < 1 || s->E < s->k || s->E_loc != s->E) return MOE_EINVAL;
+  if (s->h % 8) return MOE_EUNSUPPORTED;
+  if (s->E > kMaxExperts || s->k > kMaxK) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct ForwardLayout {
+  size_t logits, idx, w, counts, offsets, perm, inv, sched, rows, row_scales, ffn, out_rows;
+  size_t shared_off, shared_ffn, shared_out, total;
+  bool router;
+};
+
+ForwardLayout forward_layout(const moe_shape* s, moe_dtype dt, bool router) {
+  ForwardLayout L{};
+  const bool mx = dt == MOE_MXFP8;
+  const size_t R = (size_t)s->T * s->k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.router = router;
+  L.logits = router ? take((size_t)s->T * s->E * 4) : 0;
+  L.idx = router ? take(R * 4) : 0;
+  L.w = router ? take(R * 4) : 0;
+  L.counts = take((size_t)s->E_loc * 4);
+  L.offsets = take((size_t)(s->E_loc + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.sched = take(sched_workspace_bytes((int)R, s->E_loc));
+  L.rows = take(R * s->h * (mx ? 1 : 2));
+  L.row_scales = mx ? take(R * (s->h / kMxBlock)) : 0;
+  L.ffn = take(ffn_workspace_bytes((int)R, s->h, s->m, s->E_loc, mx));
+  L.out_rows = take(R * s->h * 2);
+  if (s->m_shared > 0) {
+    L.shared_off = take(2 * 4);
+    L.shared_ffn = take(ffn_workspace_bytes(s->T, s->h, s->m_shared, 1, false));
+    L.shared_out = take((size_t)s->T * s->h * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+__global__ void shared_offsets_kernel(int32_t* off, int T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape not covered by the kernels";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+  }
+  return "unknown moe_status";
+}
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+size_t moe_prepared_weight_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_expert_shape(s, dt) != MOE_OK) return 0;
+  return prepared_bytes(s->E_loc, s->h, s->m, dt == MOE_MXFP8);
+}
+
+moe_status moe_prepare_weights(const moe_shape* s, moe_dtype dt, const uint16_t* w_gate,
+                               const uint16_t* w_up, const uint16_t* w_down, void* prepared,
+                               void* stream) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(w_gate) || !ok_ptr(w_up) || !ok_ptr(w_down) || !ok_ptr(prepared)) return MOE_EINVAL;
+  return hip_status(launch_prepare_weights(w_gate, w_up, w_down, prepared, s->E_loc, s->h, s->m,
+                                           dt == MOE_MXFP8, as_stream(stream)));
+}
+
+moe_status moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                     const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
+  const moe_status st = check_router_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_opt(bias) || !ok_ptr(logits) || !ok_ptr(topk_idx) ||
+      !ok_ptr(topk_w))
+    return MOE_EINVAL;
+  const hipStream_t hs = as_stream(stream);
+  hipError_t e = launch_router_logits(x, w_router, bias, logits, s->T, s->h, s->E, hs);
+  if (e == hipSuccess) e = launch_topk_softmax(logits, topk_idx, topk_w, s->T, s->E, s->k, hs);
+  return hip_status(e);
+}
+
+size_t moe_permute_workspace_bytes(const moe_shape* s) {
+  if (!s || s->T < 1 || s->k < 1 || s->E_loc < 1) return 0;
+  return sched_workspace_bytes(s->T * s->k, s->E_loc);
+}
+
+moe_status moe_permute(const moe_shape* s, moe_dtype dt, const int32_t* assign,
+                       const uint16_t* x, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* rows, uint8_t* row_scales, void* ws, void* stream) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(assign) || !ok_ptr(x) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) ||
+      !ok_ptr(inv) || !ok_ptr(rows) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  if (dt == MOE_MXFP8 && !ok_ptr(row_scales)) return MOE_EINVAL;
+  const hipStream_t hs = as_stream(stream);
+  const int R = s->T * s->k;
+  hipError_t e = launch_schedule(assign, R, s->E_loc, counts, offsets, perm, inv, ws, hs);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (dt == MOE_MXFP8)
+    e = launch_gather_mxfp8(x, inv, reinterpret_cast<uint8_t*>(rows), row_scales, s->T, s->h,
+                            s->k, hs);
+  else
+    e = launch_gather_bf16(x, inv, reinterpret_cast<uint16_t*>(rows), s->T, s->h, s->k, hs);
+  return hip_status(e);
+}
+
+size_t moe_expert_ffn_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_expert_shape(s, dt) != MOE_OK) return 0;
+  return ffn_workspace_bytes(s->T * s->k, s->h, s->m, s->E_loc, dt == MOE_MXFP8);
+}
+
+moe_status moe_expert_ffn(const moe_shape* s, moe_dtype dt, const void* rows,
+                          const uint8_t* row_scales, const int32_t* offsets, const void* prepared,
+                          uint16_t* out_rows, void* ws, void* stream) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(rows) || !ok_ptr(offsets) || !ok_ptr(prepared) || !ok_ptr(out_rows) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  if (dt == MOE_MXFP8 && !ok_ptr(row_scales)) return MOE_EINVAL;
+  return hip_status(launch_expert_ffn(rows, row_scales, offsets, prepared, out_rows, ws,
+                                      s->T * s->k, s->h, s->m, s->E_loc, dt == MOE_MXFP8,
+                                      as_stream(stream)));
+}
+
+moe_status moe_combine(const moe_shape* s, const uint16_t* out_rows, const int32_t* inv,
+                       const float* topk_w, const uint16_t* shared_out, uint16_t* y,
+                       void* stream) {
+  if (!s || s->T < 1 || s->h < 1 || s->k < 1) return MOE_EINVAL;
+  if (s->k > kMaxK) return MOE_EUNSUPPORTED;
+  if (s->h % 8) return MOE_EUNSUPPORTED;
+  if (!ok_ptr(out_rows) || !ok_ptr(inv) || !ok_ptr(topk_w) || !ok_opt(shared_out) || !ok_ptr(y))
+    return MOE_EINVAL;
+  return hip_status(launch_combine(out_rows, inv, topk_w, shared_out, y, s->T, s->h, s->k,
+                                   as_stream(stream)));
+}
+
+size_t moe_forward_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_expert_shape(s, dt) != MOE_OK) return 0;
+  // sized for the router use (a superset of the expert-share use) when E == E_loc
+  const bool router = s->E == s->E_loc && s->E >= s->k;
+  return forward_layout(s, dt, router).total;
+}
+
+moe_status moe_forward_views(const moe_shape* s, moe_dtype dt, void* ws,
+                             moe_forward_views_t* v) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ws || !v) return MOE_EINVAL;
+  const bool router = s->E == s->E_loc && s->E >= s->k;
+  const ForwardLayout L = forward_layout(s, dt, router);
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  v->logits = router ? reinterpret_cast<float*>(b + L.logits) : nullptr;
+  v->topk_idx = router ? reinterpret_cast<int32_t*>(b + L.idx) : nullptr;
+  v->topk_w = router ? reinterpret_cast<float*>(b + L.w) : nullptr;
+  v->counts = reinterpret_cast<int32_t*>(b + L.counts);
+  v->offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  v->perm = reinterpret_cast<int32_t*>(b + L.perm);
+  v->inv = reinterpret_cast<int32_t*>(b + L.inv);
+  v->rows = b + L.rows;
+  v->row_scales = dt == MOE_MXFP8 ? b + L.row_scales : nullptr;
+  v->out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
+  v->shared_out = s->m_shared > 0 ? reinterpret_cast<uint16_t*>(b + L.shared_out) : nullptr;
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                       const uint16_t* w_router, const float* bias, const int32_t* assign,
+                       const float* assign_w, const void* prepared, const void* shared_prepared,
+                       uint16_t* y, void* ws, void* stream) {
+  moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  const bool router = w_router != nullptr;
+  if (router) {
+    st = check_router_shape(s);
+    if (st != MOE_OK) return st;
+    if (assign || assign_w || !ok_opt(bias)) return MOE_EINVAL;
+  } else {
+    if (!ok_ptr(assign) || !ok_ptr(assign_w) || bias) return MOE_EINVAL;
+  }
+  if (!ok_ptr(x) || !ok_ptr(prepared) || !ok_ptr(y) || !ok_ptr(ws)) return MOE_EINVAL;
+  if ((s->m_shared > 0) != (shared_prepared != nullptr)) return MOE_EINVAL;
+  if (shared_prepared && !ok_ptr(shared_prepared)) return MOE_EINVAL;
+
+  const bool mx = dt == MOE_MXFP8;
+  const bool router_layout = s->E == s->E_loc && s->E >= s->k;
+  const ForwardLayout L = forward_layout(s, dt, router_layout);
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  const hipStream_t hs = as_stream(stream);
+  const int T = s->T, h = s->h, k = s->k, R = T * k;
+
+  const int32_t* a_idx = assign;
+  const float* a_w = assign_w;
+  hipError_t e = hipSuccess;
+  if (router) {
+    float* logits = reinterpret_cast<float*>(b + L.logits);
+    int32_t* idx = reinterpret_cast<int32_t*>(b + L.idx);
+    float* w = reinterpret_cast<float*>(b + L.w);
+    e = launch_router_logits(x, w_router, bias, logits, T, h, s->E, hs);
+    if (e == hipSuccess) e = launch_topk_softmax(logits, idx, w, T, s->E, k, hs);
+    a_idx = idx;
+    a_w = w;
+  }
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(b + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  if (e == hipSuccess)
+    e = launch_schedule(a_idx, R, s->E_loc, counts, offsets, perm, inv, b + L.sched, hs);
+  if (e == hipSuccess) {
+    if (mx)
+      e = launch_gather_mxfp8(x, inv, b + L.rows, b + L.row_scales, T, h, k, hs);
+    else
+      e = launch_gather_bf16(x, inv, reinterpret_cast<uint16_t*>(b + L.rows), T, h, k, hs);
+  }
+  uint16_t* out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
+  if (e == hipSuccess)
+    e = launch_expert_ffn(b + L.rows, mx ? b + L.row_scales : nullptr, offsets, prepared, out_rows,
+                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs);
+  uint16_t* shared_out = nullptr;
+  if (e == hipSuccess && s->m_shared > 0) {
+    int32_t* soff = reinterpret_cast<int32_t*>(b + L.shared_off);
+    shared_out = reinterpret_cast<uint16_t*>(b + L.shared_out);
+    hipLaunchKernelGGL(shared_offsets_kernel, dim3(1), dim3(64), 0, hs, soff, T);
+    e = hipGetLastError();
+    if (e == hipSuccess)
+      e = launch_expert_ffn(x, nullptr, soff, shared_prepared, shared_out, b + L.shared_ffn, T, h,
+                            s->m_shared, 1, false, hs);
+  }
+  if (e == hipSuccess) e = launch_combine(out_rows, inv, a_w, shared_out, y, T, h, k, hs);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Internal declarations of the MI355X MoE library: device helpers shared by the kernels and the
+// host-side launchers each kernel file exports to the C-ABI front end (moe_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------------------
+// Vector types for 16-byte memory operations and MFMA operands (gfx950, wave64)
+// ------------------------------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+constexpr int kWave = 64;
+constexpr int kMxBlock = 32;
+
+// ------------------------------------------------------------------------------------------------
+// bfloat16 <-> float32
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round a finite float32 to bfloat16, to nearest with ties to even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------------------------------------
+// MX (OCP Microscaling) E4M3 elements with an E8M0 block scale
+// ------------------------------------------------------------------------------------------------
+// Block exponent of a block whose largest magnitude is amax: floor(log2 amax) - 8 (8 = exponent
+// of E4M3's largest normal, 448), clamped to [-127, 127]; -127 for an all-zero block. Read off the
+// float32 exponent field; float32 subnormal amax (< 2^-126) gives -127 after clamping too.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  uint32_t ex = (__float_as_uint(amax) >> 23) & 0xffu;  // amax >= 0
+  int s = (ex == 0u) ? -127 : (int)ex - 127 - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// 2^-s as a float (s in [-127, 127]): exact power of two. 2^127 is a normal float32.
+__device__ __forceinline__ float mx_inv_scale(int s) {
+  int e = 127 - s;  // biased exponent of 2^-s, in [0, 254]
+  return e == 0 ? __uint_as_float(0x00400000u) /* 2^-127, subnormal */
+                : __uint_as_float((uint32_t)e << 23);
+}
+
+// E4M3 code of y (already divided by the block scale): round to nearest, ties to even mantissa,
+// |y| >= 448 saturates to 448, the sign of zero is kept, NaN is never produced.
+// Normal range |y| >= 2^-6: with |y| = f * 2^e (1 <= f < 2) the mantissa is rint(|y| * 2^(3-e)) - 8,
+// a carry to 16 moves to the next binade. Below 2^-6: n = rint(|y| * 2^9), n = 8 is code 0x08.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __uint_as_float(u & 0x7fffffffu);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling, then round half to even
+  } else {
+    int e = (int)((u >> 23) & 0xffu) - 127;          // -6 .. 8
+    float scaled = a * __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // exact: a * 2^(3-e)
+    uint32_t n = (uint32_t)__builtin_rintf(scaled);  // 8 .. 16
+    if (n == 16u) { n = 8u; ++e; }
+    code = ((uint32_t)(e + 7) << 3) | (n - 8u);
+  }
+  return code | sign;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Alignment helpers for workspace carving
+// ------------------------------------------------------------------------------------------------
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+
+// ------------------------------------------------------------------------------------------------
+// Host-side launchers (each returns hipGetLastError() after enqueueing)
+// ------------------------------------------------------------------------------------------------
+// Router (moe_route_kernels.hip)
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                float* logits, int T, int h, int E, hipStream_t st);
+hipError_t launch_topk_softmax(const float* logits, int32_t* idx, float* w, int T, int E, int k,
+                               hipStream_t st);
+
+// Schedule + gather (moe_permute_kernels.hip)
+constexpr int kSchedChunk = 256;  // assignments per schedule block
+size_t sched_workspace_bytes(int R, int E_loc);
+hipError_t launch_schedule(const int32_t* assign, int R, int E_loc, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                           hipStream_t st);
+hipError_t launch_gather_bf16(const uint16_t* x, const int32_t* inv, uint16_t* rows, int T, int h,
+                              int k, hipStream_t st);
+hipError_t launch_gather_mxfp8(const uint16_t* x, const int32_t* inv, uint8_t* rows,
+                               uint8_t* scales, int T, int h, int k, hipStream_t st);
+
+// Grouped GEMMs + weight preparation (moe_gemm_kernels.hip)
+size_t ffn_workspace_bytes(int R, int h, int m, int E_loc, bool mx);
+size_t prepared_bytes(int E_loc, int h, int m, bool mx);
+hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
+                                  const uint16_t* w_down, void* prepared, int E_loc, int h, int m,
+                                  bool mx, hipStream_t st);
+hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
+                             const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
+                             int m, int E_loc, bool mx, hipStream_t st);
+
+// Combine (moe_combine_kernels.hip)
+hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,
+                          const uint16_t* shared_out, uint16_t* y, int T, int h, int k,
+                          hipStream_t st);
+
+}  // namespace moe

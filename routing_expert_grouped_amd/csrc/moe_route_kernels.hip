@@ -1,0 +1,149 @@
+// Router: logits in one fixed float32 order, then top-k and softmax renormalisation.
+//
+// Token routing is one of the parts the Mixture-of-Kittens megakernel fuses (companion news
+// digest, Merged summary; Mixture-of-Kittens page, TL;DR). The workloads define it as softmax over
+// the router logits, top-k, renormalise; the lower expert index wins a tie.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouterTokens = 8;     // tokens per wave (held in scalar registers)
+constexpr int kRouterThreads = 256;  // one expert per lane
+
+// logits[t, e] = (((0 + x[t,0] w[e,0]) + x[t,1] w[e,1]) + ...) + bias[e], float32, one fused
+// multiply-add per step. A bf16 x bf16 product is exact in float32, so each step rounds once and
+// the order is the written left-to-right one: no split over h, no tree.
+//
+// Layout: each lane owns one expert (its router row is contiguous in h and streamed 8 values per
+// 16-byte load); each workgroup owns kRouterTokens tokens whose x values are wave-uniform, so they
+// are fetched with scalar loads and fed to the FMAs as scalar operands. The work is bound by the
+// float32 FMA rate, 2*T*h*E flop.
+__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int h, int E) {
+  const int e = blockIdx.y * kRouterThreads + threadIdx.x;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
+  const uint4* wrow = reinterpret_cast<const uint4*>(w + (size_t)e_ld * h);
+  const uint4* xrow[kRouterTokens];
+#pragma unroll
+  for (int tt = 0; tt < kRouterTokens; ++tt) {
+    int t = t0 + tt < T ? t0 + tt : T - 1;
+    xrow[tt] = reinterpret_cast<const uint4*>(x + (size_t)t * h);
+  }
+  float acc[kRouterTokens];
+#pragma unroll
+  for (int tt = 0; tt < kRouterTokens; ++tt) acc[tt] = 0.0f;
+
+  const int nvec = h / 8;
+  for (int v = 0; v < nvec; ++v) {
+    const uint4 wv = wrow[v];
+    const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                         bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+#pragma unroll
+    for (int tt = 0; tt < kRouterTokens; ++tt) {
+      const uint4 xv = xrow[tt][v];
+      const float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
+                           bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[tt] = __builtin_fmaf(xf[q], wf[q], acc[tt]);
+    }
+  }
+  if (e < E) {
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < kRouterTokens; ++tt) {
+      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = bias ? acc[tt] + b : acc[tt];
+    }
+  }
+}
+
+// "a ranks before b": larger logit first, then the lower expert index.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+constexpr int kTopkMaxPerLane = 16;  // E <= 1024
+
+// One wave per token. Each lane holds the logits of experts lane, lane+64, ...; k rounds of a
+// wave-wide arg-max under (logit desc, index asc) pick the experts in rank order. -0.0 is made
+// +0.0 on load so both zeros tie. Weights: softmax over the k selected logits,
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), summed in slot order.
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits,
+                                                           int32_t* __restrict__ idx,
+                                                           float* __restrict__ wout, int T, int E,
+                                                           int k) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+  const float* row = logits + (size_t)t * E;
+  float v[kTopkMaxPerLane];
+  const int per_lane = (E + 63) / 64;
+#pragma unroll
+  for (int q = 0; q < kTopkMaxPerLane; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = (q < per_lane && e < E) ? row[e] + 0.0f : -__builtin_inff();
+  }
+  unsigned taken = 0u;  // bit q: v[q] already selected (or absent)
+#pragma unroll
+  for (int q = 0; q < kTopkMaxPerLane; ++q)
+    if (!(q < per_lane && lane + 64 * q < E)) taken |= 1u << q;
+
+  float sel_v = 0.0f;  // lane j < k ends up holding the j-th selected logit
+  int sel_i = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < kTopkMaxPerLane; ++q) {
+      if (!(taken & (1u << q)) && ranks_before(v[q], lane + 64 * q, bv, bi)) {
+        bv = v[q];
+        bi = lane + 64 * q;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    // every lane now holds the winner (bv, bi)
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      sel_v = bv;
+      sel_i = bi;
+    }
+  }
+  const float l0 = __shfl(sel_v, 0);
+  const float ex = lane < k ? expf(sel_v - l0) : 0.0f;
+  // fixed-order sum over the k slots (slot 0 first), identical in every lane
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += __shfl(ex, j);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = sel_i;
+    wout[(size_t)t * k + lane] = ex / sum;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                float* logits, int T, int h, int E, hipStream_t st) {
+  dim3 grid((T + kRouterTokens - 1) / kRouterTokens, (E + kRouterThreads - 1) / kRouterThreads);
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRouterThreads), 0, st, x, w_router, bias,
+                     logits, T, h, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_softmax(const float* logits, int32_t* idx, float* w, int T, int E, int k,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(topk_softmax_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, idx, w, T,
+                     E, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

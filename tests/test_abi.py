@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/moe.h declares, its
+size queries are consistent, and invalid arguments are rejected on the host before anything is
+enqueued (every call below fails validation, so no HIP work is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from routing_expert_grouped_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from routing_expert_grouped_amd import build
+        build.build(verbose=False)
+    return _lib
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    L = lib.load()
+    declared = _declared_functions()
+    assert sorted(lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(lib):
+    L = lib.load()
+    assert L.moe_abi_version() == 1
+    for code in range(4):
+        assert L.moe_status_string(code).decode().startswith("MOE_")
+
+
+def _shape(lib, **kw):
+    base = dict(T=64, h=256, m=128, E=8, k=2, E_loc=8, m_shared=0)
+    base.update(kw)
+    return lib.MoeShape(**base)
+
+
+def test_size_queries(lib):
+    L = lib.load()
+    s = _shape(lib)
+    R, h, m, E = 128, 256, 128, 8
+    assert L.moe_prepared_weight_bytes(ctypes.byref(s), 0) == 3 * E * h * m * 2
+    mx = _shape(lib, m=256)
+    n = L.moe_prepared_weight_bytes(ctypes.byref(mx), 1)
+    assert n >= 3 * E * h * 256 * (1 + 1 / 32)
+    assert L.moe_forward_workspace_bytes(ctypes.byref(s), 0) > R * h * 4
+    assert L.moe_expert_ffn_workspace_bytes(ctypes.byref(s), 0) >= R * m * 2
+    assert L.moe_permute_workspace_bytes(ctypes.byref(s)) > 0
+    # rejected shapes size to 0
+    assert L.moe_prepared_weight_bytes(ctypes.byref(_shape(lib, h=200)), 0) == 0
+    assert L.moe_forward_workspace_bytes(ctypes.byref(_shape(lib, k=0)), 0) == 0
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: each call below fails validation first
+
+
+def test_route_validation(lib):
+    L = lib.load()
+    P = FAKE
+    ok = _shape(lib)
+    assert L.moe_route(None, P, P, None, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(_shape(lib, k=9)), P, P, None, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(_shape(lib, E=8, E_loc=4)), P, P, None, P, P, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), None, P, None, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), P + 2, P, None, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), P, P, P + 4, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(_shape(lib, E=2000, E_loc=2000)), P, P, None, P, P, P,
+                       None) == lib.MOE_EUNSUPPORTED
+    assert L.moe_route(ctypes.byref(_shape(lib, E=40, E_loc=40, k=17)), P, P, None, P, P, P,
+                       None) == lib.MOE_EUNSUPPORTED
+
+
+def test_expert_path_validation(lib):
+    L = lib.load()
+    P = FAKE
+    ok = _shape(lib)
+    # permute
+    assert L.moe_permute(ctypes.byref(ok), 0, None, P, P, P, P, P, P, None, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_permute(ctypes.byref(_shape(lib, m=256)), 1, P, P, P, P, P, P, P, None, P,
+                         None) == lib.MOE_EINVAL  # MXFP8 needs row_scales
+    assert L.moe_permute(ctypes.byref(ok), 7, P, P, P, P, P, P, P, None, P, None) == \
+        lib.MOE_EINVAL  # unknown dtype
+    # expert ffn: shapes the kernels do not tile
+    assert L.moe_expert_ffn(ctypes.byref(_shape(lib, h=192)), 0, P, None, P, P, P, P, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_expert_ffn(ctypes.byref(_shape(lib, m=96)), 0, P, None, P, P, P, P, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_expert_ffn(ctypes.byref(_shape(lib, h=240)), 1, P, P, P, P, P, P, None) == \
+        lib.MOE_EINVAL  # MXFP8 needs h % 32 == 0
+    assert L.moe_expert_ffn(ctypes.byref(_shape(lib, m=128)), 1, P, P, P, P, P, P, None) == \
+        lib.MOE_EUNSUPPORTED  # MXFP8 K chunks are 256 wide
+    assert L.moe_expert_ffn(ctypes.byref(ok), 0, P, None, P, None, P, P, None) == lib.MOE_EINVAL
+    # combine
+    assert L.moe_combine(ctypes.byref(_shape(lib, k=17)), P, P, P, None, P, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_combine(ctypes.byref(ok), P, P, None, None, P, None) == lib.MOE_EINVAL
+    # forward: router and share arguments are exclusive; shared expert consistency
+    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, P, P, P, None, P, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_forward(ctypes.byref(ok), 0, P, None, None, None, None, P, None, P, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_forward(ctypes.byref(_shape(lib, m_shared=128)), 0, P, P, None, None, None, P,
+                         None, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, None, None, P, None, P, None, None) == \
+        lib.MOE_EINVAL
+    # prepare weights
+    assert L.moe_prepare_weights(ctypes.byref(ok), 0, P, P, None, P, None) == lib.MOE_EINVAL
+
+
+def test_views_are_host_arithmetic(lib):
+    L = lib.load()
+    s = _shape(lib)
+    v = lib.MoeForwardViews()
+    base = 1 << 30
+    assert L.moe_forward_views(ctypes.byref(s), 0, base, ctypes.byref(v)) == lib.MOE_OK
+    ptrs = [getattr(v, n) for n, _ in lib.MoeForwardViews._fields_ if getattr(v, n)]
+    assert all(p % 256 == 0 and base <= p < base + L.moe_forward_workspace_bytes(
+        ctypes.byref(s), 0) for p in ptrs)
+    assert v.row_scales is None and v.shared_out is None and v.logits is not None

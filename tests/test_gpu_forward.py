@@ -1,0 +1,77 @@
+"""GPU parity of moe_forward (the whole layer) on scaled-down versions of the five workloads:
+routing and schedule bit-exact, output within tolerance, and two runs bitwise identical."""
+import numpy as np
+import pytest
+
+import moe_inputs as I
+from oracle import moe as M
+from tests._gpu_helpers import (BF16_TOL, MX_TOL, dev, dev_bf16, host_bf16_bits,
+                                host_f64_from_bf16, normwise_err, note, poisoned, require_gpu,
+                                torch)
+
+pytestmark = pytest.mark.gpu
+
+SCALED = {
+    "tiny": dict(),
+    "dsv4pro": dict(T=256, h=512, m=384),
+    "qwen397": dict(T=320, h=512, m=128, E=64, E_loc=64),
+    "kimi": dict(T=192, h=512, m=256, m_shared=256),
+    "glm52": dict(T=300, h=768, m=512, E=64, E_loc=64),
+}
+
+
+def run_forward(G, wl, inp, weights, shared=None, y=None, ws=None):
+    sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared)
+    prepared = G.moe_prepare_weights(sh, wl.dtype, *weights)
+    shared_prep = None
+    if shared is not None:
+        ssh = G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1)
+        shared_prep = G.moe_prepare_weights(ssh, "bf16", *shared)
+    kw = {}
+    if wl.mode == "router":
+        kw["w_router"] = dev_bf16(inp["w_router"])
+        kw["bias"] = None if inp["bias"] is None else dev(inp["bias"])
+    else:
+        kw["assign"] = dev(inp["assign"])
+        kw["assign_w"] = dev(inp["assign_w"])
+    y, ws = G.moe_forward(sh, wl.dtype, dev_bf16(inp["x"]), prepared,
+                          shared_prepared=shared_prep, y=y, ws=ws, **kw)
+    return sh, y, ws
+
+
+@pytest.mark.parametrize("name", list(SCALED))
+def test_forward_scaled_workloads(name):
+    G = require_gpu()
+    base = I.get(name)
+    wl = I.scaled(base, **SCALED[name]) if SCALED[name] else base
+    note(f"forward {wl.describe()}")
+    inp = I.make_inputs(wl, seed=0)
+    wts = [I.expert_weights(wl, e) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    shared = None
+    if wl.m_shared:
+        sw = I.shared_weights(wl)
+        shared = tuple(dev_bf16(v) for v in sw)
+    y0 = poisoned((wl.T, wl.h), torch.bfloat16)
+    sh, y, ws = run_forward(G, wl, inp, weights, shared, y=y0)
+    torch.cuda.synchronize()
+    ref = M.layer_forward(wl, inp, lambda e: wts[e],
+                          shared_weights=I.shared_weights(wl) if wl.m_shared else None)
+    v = G.moe_forward_views(sh, wl.dtype, ws)
+    if wl.mode == "router":
+        assert np.array_equal(v["logits"].cpu().numpy().view(np.uint32),
+                              ref["logits"].view(np.uint32))
+        assert np.array_equal(v["topk_idx"].cpu().numpy(), ref["idx"])
+        assert np.allclose(v["topk_w"].cpu().numpy(), ref["w"], rtol=1e-6, atol=0)
+    for key in ("counts", "offsets", "perm", "inv"):
+        assert np.array_equal(v[key].cpu().numpy(), ref[key]), key
+    got = host_f64_from_bf16(y)
+    assert np.isfinite(got).all()
+    err = normwise_err(got, ref["y"])
+    note(f"  normwise error {err:.3e}")
+    assert err <= (MX_TOL if wl.dtype == "mxfp8" else BF16_TOL)
+    # run again into a fresh poisoned buffer and a fresh workspace: bitwise identical
+    y1 = poisoned((wl.T, wl.h), torch.bfloat16)
+    _, y1, _ = run_forward(G, wl, inp, weights, shared, y=y1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y1))
