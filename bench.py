@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""MoE layer forward throughput on one MI355X, with the dominant kernel's roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_forward of the whole hot path over one batch of seeded synthetic inputs
+(expert shares: schedule, gather, grouped SwiGLU GEMMs, combine; full layers: router and top-k
+first). The default workload is the DeepSeek-V4-Pro-shaped expert share of one GPU at expert
+parallelism 64 (2,048 source tokens, 6 local experts, top-6, h = 7168, m = 3072, BF16).
+
+Inputs live in HBM before the timed region starts. The K timed steps run back to back between two
+device synchronisations; each step records HIP events at its stage boundaries on the library's
+stream, which gives every kernel's duration live. One JSON line is printed.
+
+The CPU baseline times the oracle (oracle/, float64 NumPy) on a bounded sample of the same
+workload's tokens on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MoE layer fwd tokens/s on 1 GPU + grouped-GEMM % MFMA peak (BF16/MXFP8)"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}  # MI355X dense matrix peaks
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv4pro")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256,
+                    help="tokens of the oracle's timed sample (0 disables the CPU baseline)")
+    return ap.parse_args()
+
+
+def layer_flops(wl) -> dict:
+    R = wl.T * wl.k
+    f = {
+        "gemm1": 4.0 * R * wl.h * wl.m,  # gate and up: 2 * R * h * (2m)
+        "gemm2": 2.0 * R * wl.m * wl.h,
+        "router": 2.0 * wl.T * wl.h * wl.E if wl.mode == "router" else 0.0,
+        "shared": 6.0 * wl.T * wl.h * wl.m_shared,
+    }
+    f["total"] = sum(f.values())
+    return f
+
+
+def stage_bytes(wl) -> dict:
+    """Algorithmic HBM bytes of the bandwidth-bound stages (each byte moved once)."""
+    R, T, h, k = wl.T * wl.k, wl.T, wl.h, wl.k
+    mx = wl.dtype == "mxfp8"
+    row_b = h * (1 + 1 / 32) if mx else 2 * h
+    return {
+        "gather": T * h * 2 + R * row_b + R * 4,                       # read x once, write R rows
+        "combine": R * h * 2 + R * 8 + T * h * 2 + (T * h * 2 if wl.m_shared else 0),
+        "topk": T * wl.E * 4 + R * 8 if wl.mode == "router" else 0,
+    }
+
+
+def cpu_baseline(wl, inp, weights_host, shared_host, n_tokens: int) -> dict:
+    from oracle import moe as M  # the oracle is the baseline leg only
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    tokens = np.arange(min(n_tokens, wl.T))
+    t0 = time.perf_counter()
+    M.token_outputs(wl, inp, tokens, weights_host.__getitem__, shared_host)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {len(tokens)} of {wl.T} tokens of the same workload through "
+                      f"oracle.moe.token_outputs (float64 NumPy, routing + every selected "
+                      f"expert's SwiGLU FFN + combine), {dt:.1f} s wall"}
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this build has no multi-GPU path; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import moe_inputs as I
+    import routing_expert_grouped_amd as G
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    wl = I.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = I.make_inputs(wl, seed=args.seed)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = bf16(inp["x"])
+    wg, wu, wd = I.torch_expert_weights(wl, dev, seed=args.seed)
+    sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared)
+    prepared = G.moe_prepare_weights(sh, wl.dtype, wg, wu, wd)
+    shared_prep = None
+    shared_w = None
+    if wl.m_shared:
+        shared_w = I.torch_shared_weights(wl, dev, seed=args.seed)
+        ssh = G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1)
+        shared_prep = G.moe_prepare_weights(ssh, "bf16", *shared_w)
+    kw = {}
+    if wl.mode == "router":
+        kw["w_router"] = bf16(inp["w_router"])
+        kw["bias"] = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev)
+    else:
+        kw["assign"] = torch.from_numpy(inp["assign"]).to(dev)
+        kw["assign_w"] = torch.from_numpy(inp["assign_w"]).to(dev)
+    y = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(G.moe_forward_workspace_bytes(sh, wl.dtype), dtype=torch.uint8, device=dev)
+    events = [G.HipEvents() for _ in range(args.steps)]
+    warm_ev = G.HipEvents()
+
+    def step(ev):
+        G.moe_forward_profiled(sh, wl.dtype, x, prepared, ev, shared_prepared=shared_prep, y=y,
+                               ws=ws, **kw)
+
+    for _ in range(args.warmup):
+        step(warm_ev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    stages = {k: 0.0 for k in G.STAGES}
+    for ev in events:
+        for k, v in ev.stage_ms().items():
+            stages[k] += v / args.steps
+    for ev in events + [warm_ev]:
+        ev.close()
+
+    fl = layer_flops(wl)
+    by = stage_bytes(wl)
+    peak = PEAK_TFLOPS[wl.dtype]
+    g1_ms = stages["gemm1_gate_up_swiglu"]
+    g2_ms = stages["gemm2_down"]
+    g1_tf = fl["gemm1"] / (g1_ms * 1e-3) / 1e12
+    gemm_tf = (fl["gemm1"] + fl["gemm2"]) / ((g1_ms + g2_ms) * 1e-3) / 1e12
+    tokens_per_s = wl.T / (ms_per_step * 1e-3)
+
+    def gbs(name):
+        ms = stages[name]
+        return round(by[name] / (ms * 1e-3) / 1e9, 1) if ms > 0 and by[name] else None
+
+    baseline = None
+    if args.cpu_sample_tokens > 0:
+        def host_bits(t):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        class HostWeights(dict):
+            """Expert weights copied to the host on first use (all of them up front for an
+            expert share, which holds only a few experts)."""
+
+            def __missing__(self, e):
+                self[e] = tuple(host_bits(t[e]) for t in (wg, wu, wd))
+                return self[e]
+
+        host = HostWeights()
+        if wl.mode == "share":
+            for e in range(wl.E_loc):
+                host[e]
+        sh_host = tuple(host_bits(t) for t in shared_w) if shared_w is not None else None
+        baseline = cpu_baseline(wl, inp, host, sh_host, args.cpu_sample_tokens)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; random-init expert weights of the stated shapes)",
+        "config": {"workload": wl.name, "T": wl.T, "h": wl.h, "m": wl.m, "E": wl.E,
+                   "E_loc": wl.E_loc, "k": wl.k, "routed_rows": wl.T * wl.k,
+                   "mode": wl.mode, "m_shared": wl.m_shared},
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM-1 (gate/up + SwiGLU epilogue)",
+                     "achieved": round(g1_tf, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(g1_tf / peak, 4), "traffic": None},
+        "grouped_gemm_mfma_frac": round(gemm_tf / peak, 4),
+        "layer_tflops": round(fl["total"] / (ms_per_step * 1e-3) / 1e12, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stages_gbs": {k: gbs(k) for k in ("gather", "combine", "topk")},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

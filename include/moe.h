@@ -173,6 +173,19 @@ moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                        const float* assign_w, const void* prepared, const void* shared_prepared,
                        uint16_t* y, void* ws, void* stream);
 
+/* Profiling variant of moe_forward: the same work on the same stream, plus hipEventRecord of the
+ * caller's events at the stage boundaries, so a caller can time each kernel live:
+ *   ev[0] router logits ev[1] top-k ev[2] schedule ev[3] gather ev[4] tile table ev[5] GEMM-1
+ *   ev[6] GEMM-2 ev[7] shared expert ev[8] combine ev[9]
+ * `events` is a host array of MOE_PROFILE_EVENTS hipEvent_t handles created by the caller
+ * (hipEventCreate); stages that do not run for a shape have back-to-back events. */
+#define MOE_PROFILE_EVENTS 10
+moe_status moe_forward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                const uint16_t* w_router, const float* bias,
+                                const int32_t* assign, const float* assign_w,
+                                const void* prepared, const void* shared_prepared, uint16_t* y,
+                                void* ws, void* const* events /* host */, void* stream);
+
 /* Addresses of the intermediates moe_forward leaves in `ws` (device pointers into ws; NULL when a
  * buffer does not exist for this shape). Host-only arithmetic, nothing is enqueued. */
 typedef struct {

@@ -15,13 +15,15 @@ from typing import Optional
 
 import torch
 
-from ._lib import (MOE_BF16, MOE_MXFP8, MoeError, MoeForwardViews, MoeShape, check, load)
+from ._lib import (MOE_BF16, MOE_MXFP8, MOE_PROFILE_EVENTS, STAGES, MoeError, MoeForwardViews,
+                   MoeShape, check, load)
 
 __all__ = [
     "MOE_BF16", "MOE_MXFP8", "MoeError", "make_shape", "dtype_code",
     "moe_prepared_weight_bytes", "moe_prepare_weights", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
-    "moe_forward_workspace_bytes", "moe_forward", "moe_forward_views",
+    "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
+    "HipEvents", "STAGES",
 ]
 
 
@@ -187,6 +189,63 @@ def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, a
         _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
         _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
         _ptr(ws, "ws"), _stream(stream)))
+    return y, ws
+
+
+class HipEvents:
+    """MOE_PROFILE_EVENTS timing events from the HIP runtime (hipEventCreate / ElapsedTime)."""
+
+    def __init__(self, n: int = MOE_PROFILE_EVENTS):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def synchronize(self) -> None:
+        self._hip.hipEventSynchronize(self.handles[self.n - 1])
+
+    def stage_ms(self) -> dict:
+        """Milliseconds of each stage of the last profiled forward."""
+        return {name: self.elapsed_ms(i, i + 1) for i, name in enumerate(STAGES)}
+
+    def close(self) -> None:
+        for i in range(self.n):
+            if self.handles[i]:
+                self._hip.hipEventDestroy(self.handles[i])
+                self.handles[i] = None
+
+
+def moe_forward_profiled(shape: MoeShape, dtype, x, prepared, events: HipEvents, w_router=None,
+                         bias=None, assign=None, assign_w=None, shared_prepared=None, y=None,
+                         ws=None, stream=None):
+    """moe_forward plus HIP events at the stage boundaries (events.stage_ms() afterwards)."""
+    dt = dtype_code(dtype)
+    T, h, k = shape.T, shape.h, shape.k
+    dev = _dev(x)
+    y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
+    n = moe_forward_workspace_bytes(shape, dt)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    check("moe_forward_profiled", load().moe_forward_profiled(
+        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h), _ptr(w_router, "w_router"),
+        _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
+        _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
+        _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
+        _ptr(ws, "ws"), ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
     return y, ws
 
 

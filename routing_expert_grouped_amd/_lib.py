@@ -22,8 +22,12 @@ EXPORTS = [
     "moe_permute_workspace_bytes", "moe_permute",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
     "moe_combine",
-    "moe_forward_workspace_bytes", "moe_forward", "moe_forward_views",
+    "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
 ]
+
+MOE_PROFILE_EVENTS = 10
+STAGES = ["router_logits", "topk", "schedule", "gather", "tile_table", "gemm1_gate_up_swiglu",
+          "gemm2_down", "shared_expert", "combine"]
 
 
 class MoeShape(ctypes.Structure):
@@ -71,6 +75,7 @@ def load() -> ctypes.CDLL:
         "moe_combine": (I, [S, P, P, P, P, P, P]),
         "moe_forward_workspace_bytes": (Z, [S, I]),
         "moe_forward": (I, [S, I, P, P, P, P, P, P, P, P, P, P]),
+        "moe_forward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P]),
         "moe_forward_views": (I, [S, I, P, ctypes.POINTER(MoeForwardViews)]),
     }
     for name, (res, args) in sig.items():

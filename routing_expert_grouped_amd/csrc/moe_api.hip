@@ -216,10 +216,14 @@ moe_status moe_forward_views(const moe_shape* s, moe_dtype dt, void* ws,
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
-                       const uint16_t* w_router, const float* bias, const int32_t* assign,
-                       const float* assign_w, const void* prepared, const void* shared_prepared,
-                       uint16_t* y, void* ws, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                        const uint16_t* w_router, const float* bias, const int32_t* assign,
+                        const float* assign_w, const void* prepared, const void* shared_prepared,
+                        uint16_t* y, void* ws, const hipEvent_t* ev, void* stream) {
   moe_status st = check_expert_shape(s, dt);
   if (st != MOE_OK) return st;
   const bool router = w_router != nullptr;
@@ -244,31 +248,41 @@ moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
   const int32_t* a_idx = assign;
   const float* a_w = assign_w;
   hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[i], hs);
+  };
+  mark(0);
   if (router) {
     float* logits = reinterpret_cast<float*>(b + L.logits);
     int32_t* idx = reinterpret_cast<int32_t*>(b + L.idx);
     float* w = reinterpret_cast<float*>(b + L.w);
     e = launch_router_logits(x, w_router, bias, logits, T, h, s->E, hs);
+    mark(1);
     if (e == hipSuccess) e = launch_topk_softmax(logits, idx, w, T, s->E, k, hs);
     a_idx = idx;
     a_w = w;
+  } else {
+    mark(1);
   }
+  mark(2);
   int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
   int32_t* perm = reinterpret_cast<int32_t*>(b + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
   if (e == hipSuccess)
     e = launch_schedule(a_idx, R, s->E_loc, counts, offsets, perm, inv, b + L.sched, hs);
+  mark(3);
   if (e == hipSuccess) {
     if (mx)
       e = launch_gather_mxfp8(x, inv, b + L.rows, b + L.row_scales, T, h, k, hs);
     else
       e = launch_gather_bf16(x, inv, reinterpret_cast<uint16_t*>(b + L.rows), T, h, k, hs);
   }
+  mark(4);
   uint16_t* out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
   if (e == hipSuccess)
     e = launch_expert_ffn(b + L.rows, mx ? b + L.row_scales : nullptr, offsets, prepared, out_rows,
-                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs);
+                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs, ev ? ev + 5 : nullptr);
   uint16_t* shared_out = nullptr;
   if (e == hipSuccess && s->m_shared > 0) {
     int32_t* soff = reinterpret_cast<int32_t*>(b + L.shared_off);
@@ -279,8 +293,34 @@ moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
       e = launch_expert_ffn(x, nullptr, soff, shared_prepared, shared_out, b + L.shared_ffn, T, h,
                             s->m_shared, 1, false, hs);
   }
+  mark(8);
   if (e == hipSuccess) e = launch_combine(out_rows, inv, a_w, shared_out, y, T, h, k, hs);
+  mark(9);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                       const uint16_t* w_router, const float* bias, const int32_t* assign,
+                       const float* assign_w, const void* prepared, const void* shared_prepared,
+                       uint16_t* y, void* ws, void* stream) {
+  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y, ws,
+                      nullptr, stream);
+}
+
+moe_status moe_forward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                const uint16_t* w_router, const float* bias,
+                                const int32_t* assign, const float* assign_w,
+                                const void* prepared, const void* shared_prepared, uint16_t* y,
+                                void* ws, void* const* events, void* stream) {
+  if (!events) return MOE_EINVAL;
+  for (int i = 0; i < MOE_PROFILE_EVENTS; ++i)
+    if (!events[i]) return MOE_EINVAL;
+  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y, ws,
+                      reinterpret_cast<const hipEvent_t*>(events), stream);
 }
 
 }  // extern "C"

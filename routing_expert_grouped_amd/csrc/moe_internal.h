@@ -114,9 +114,11 @@ size_t prepared_bytes(int E_loc, int h, int m, bool mx);
 hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
                                   const uint16_t* w_down, void* prepared, int E_loc, int h, int m,
                                   bool mx, hipStream_t st);
+// ev (optional): three events recorded after the tile table, GEMM-1 and GEMM-2
 hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
                              const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
-                             int m, int E_loc, bool mx, hipStream_t st);
+                             int m, int E_loc, bool mx, hipStream_t st,
+                             const hipEvent_t* ev = nullptr);
 
 // Combine (moe_combine_kernels.hip)
 hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,

@@ -17,9 +17,13 @@ CASES = [
     ("bf16", [16, 0, 40, 200], 256, 128),
     ("bf16", [1, 129, 0, 300, 127, 2], 384, 192),
     ("bf16", [517], 512, 256),
+    ("bf16", [300, 0, 700, 31], 256, 256),     # 256-row tiles, several experts
+    ("bf16", [2000, 513], 1024, 512),          # many K stages, several N tiles
     ("mxfp8", [16, 0, 40, 200], 256, 256),
     ("mxfp8", [1, 129, 0, 300, 127, 2], 512, 256),
     ("mxfp8", [0, 0, 259], 768, 512),
+    ("mxfp8", [600, 0, 301], 512, 256),        # 256-row tiles
+    ("mxfp8", [1500, 700], 1024, 512),
 ]
 
 
