@@ -37,9 +37,26 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv4pro")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="tokens of the oracle's timed sample (0 disables the CPU baseline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain device-to-device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n}), flush=True)
+    return 0
 
 
 def layer_flops(wl) -> dict:
@@ -87,6 +104,8 @@ def cpu_baseline(wl, inp, weights_host, shared_host, n_tokens: int) -> dict:
 
 def main() -> int:
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "

@@ -315,25 +315,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 // AccVGPR file). K advances RB bytes per stage (RB = 64 or 128: 32/64 bf16 or 64/128 E4M3).
 //
 // Operands go global -> LDS directly (global_load_lds_dwordx4), NS stages deep, so no VGPRs hold
-// staged data. The compiler does not order these asynchronous LDS writes against the LDS reads, so
-// the pipeline waits explicitly: before stage kt is read, s_waitcnt vmcnt(n) with n the exact
-// number of loads this wave issued after stage kt's (vmcnt(0) near the end, which is always safe),
-// then a barrier so every wave's part of the stage is in LDS and no wave still reads the buffer the
-// next load overwrites.
+// staged data. The compiler does not order these asynchronous LDS writes against LDS reads, so the
+// pipeline waits explicitly: before stage j is read, s_waitcnt vmcnt(n) where n is the exact
+// number of loads this wave issued after stage j's (counted at run time from the fixed issue
+// order), then a barrier, so every wave's part of stage j is in LDS and no wave still reads the
+// buffer the next DMA overwrites.
+//
+// Fragments are software-pipelined one k-step ahead: the LDS reads of k-step t+1 are in flight
+// while the MFMAs of k-step t run, and the wait/barrier for the next stage sits inside the last
+// k-step of the current one, so the first fragments of a stage are read before its MFMAs start.
 //
 // LDS rows are RB bytes, split into 16-byte slots; slot p of row r holds logical chunk p ^ f(r)
 // (f(r) = ((r >> 1) ^ (r >> 2)) & 3 for RB = 64, (r ^ (r >> 3)) & 7 for RB = 128), which spreads
 // the lanes that read one logical chunk of consecutive rows over distinct bank groups for both
 // 8-lane and 16-lane LDS phases. The swizzle is applied on the global side: the DMA writes a
-// wave's 64 lanes to 1 KB of consecutive LDS, and each lane fetches the global chunk that belongs
-// in its slot.
+// wave's 64 lanes to 1 KB of consecutive LDS, and each lane fetches the chunk for its slot.
 //
-// Work order: workgroup L runs on XCD L % 8; the valid tiles are split into 8 contiguous ranges,
-// one per XCD, and inside a range the order walks 4 consecutive M tiles for each N tile, so the 32
-// workgroups an XCD runs at once share 4 row panels and 8 weight panels in its L2.
+// Work order: the M tiles are cut into bands of 8; all XCDs work on the same band at the same
+// time (so the band's rows and its experts' weights stay in the MALL), and inside a band XCD x
+// takes the x-th eighth of the band's tiles in N-major order, i.e. a block of about Nt/8 weight
+// panels by 8 row panels that its 32 CUs share through its L2. Workgroup L runs on XCD L % 8.
 // ------------------------------------------------------------------------------------------------
 constexpr int kBigBN = 256;
-constexpr int kGroupM = 4;
+constexpr int kBandM = 8;
 
 template <int RB>
 __device__ __forceinline__ int big_swz(int row) {
@@ -355,7 +359,18 @@ __device__ __forceinline__ void wait_vmcnt_fenced() {
   wait_vmcnt<N>();
 }
 
-// every LDS read of this wave has returned, then all waves meet; no memory access moves across
+// vmcnt(n) for a wave-uniform run-time n in [LO, HI], by binary dispatch on the immediate
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vmcnt_range<MID, HI>(n);
+    else wait_vmcnt_range<LO, MID - 1>(n);
+  }
+}
+
 // 16-byte global -> LDS DMA of one lane (the wave's 64 lanes fill 1 KB of consecutive LDS from
 // `l`). The builtin only exists in the device pass; the host pass, which only needs the kernel's
 // launch stub, must not see it (it would drop the stub).
@@ -368,6 +383,7 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
 #endif
 }
 
+// every LDS read of this wave has returned, then all waves meet; no memory access moves across
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
@@ -382,18 +398,15 @@ __device__ __forceinline__ void lds_barrier() {
 #ifndef MOE_BIG_NS_BF16
 #define MOE_BIG_NS_BF16 2
 #endif
+#ifndef MOE_BIG_NS_BF16_128
+#define MOE_BIG_NS_BF16_128 3  // 128-row BF16 tiles: 3 stages of 48 KB
+#endif
 #ifndef MOE_BIG_RB_MX
 #define MOE_BIG_RB_MX 128
 #endif
 #ifndef MOE_BIG_NS_MX
-#define MOE_BIG_NS_MX 2
+#define MOE_BIG_NS_MX 3
 #endif
-template <bool MX, int BM>
-struct BigCfg {
-  static constexpr int RB = MX ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16;
-  static constexpr int NS = MX ? MOE_BIG_NS_MX : MOE_BIG_NS_BF16;
-  static_assert(NS * (kBigBN + BM) * RB <= 160 * 1024, "LDS budget");
-};
 
 template <bool MX, bool SWIGLU, int BM, int RB, int NS>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
@@ -405,26 +418,40 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   constexpr int LOADS = ROWS * RB / 16 / 256;    // 16-byte DMA loads per thread per stage
   constexpr int SLOTS = RB / 16;
   constexpr int SPS = MX ? RB / 64 : RB / 32;    // MFMA k-steps per stage
-  constexpr int PER_CHUNK = MX ? 4 / SPS : 1;    // stages per 256-element MX chunk
+  constexpr int PC = MX ? 4 / SPS : 1;           // stages per 256-element MX chunk
   constexpr int NSC = MX ? NI + NJ : 0;          // scale loads per chunk
-  static_assert(LOADS * (NS - 2) + NSC < 64, "vmcnt range");
-  static_assert(!MX || NS - 1 <= PER_CHUNK, "scale prefetch distance");
+  constexpr int MAXN = LOADS * (NS - 2);
+  static_assert(MAXN < 64 && NS <= 5, "vmcnt range");
+  static_assert(!MX || PC >= 2, "the scale prefetch needs two stages per chunk");
+  static_assert(MX || SPS % 2 == 0, "fragment double buffer alternates within a stage");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
 
-  // ---- which tile: XCD-contiguous ranges, grouped M order
+  // ---- which tile: band b of 8 M tiles, XCD x takes the x-th eighth of it (N-major)
   const int mt_total = *p.tile_count;
   const int Nt = p.N / BN;
-  const int total = mt_total * Nt;
-  const int per_xcd = (total + 7) >> 3;
-  const int L = blockIdx.x;
-  if ((L >> 3) >= per_xcd) return;
-  const int logical = (L & 7) * per_xcd + (L >> 3);
-  if (logical >= total) return;
-  const int gm0 = (logical / (kGroupM * Nt)) * kGroupM;
-  const int gsz = min(kGroupM, mt_total - gm0);
-  const int rr = logical - gm0 * Nt;
-  const int nt = rr / gsz;
-  const int2 te = p.tiles[gm0 + rr % gsz];
+  const int x = blockIdx.x & 7;
+  int jx = blockIdx.x >> 3;  // this workgroup's index among the XCD's workgroups
+  const int nb_full = mt_total / kBandM;
+  const int tb_full = kBandM * Nt;
+  const int share_full = ((x + 1) * tb_full >> 3) - (x * tb_full >> 3);
+  int band, band_rows, tb;
+  if (jx < nb_full * share_full) {
+    band = jx / share_full;
+    jx -= band * share_full;
+    band_rows = kBandM;
+    tb = tb_full;
+  } else {
+    jx -= nb_full * share_full;
+    band = nb_full;
+    band_rows = mt_total - nb_full * kBandM;
+    tb = band_rows * Nt;
+    const int share_last = ((x + 1) * tb >> 3) - (x * tb >> 3);
+    if (jx >= share_last) return;  // surplus workgroup: leaves before any barrier
+  }
+  const int pos = (x * tb >> 3) + jx;
+  const int nt = pos / band_rows;
+  const int2 te = p.tiles[band * kBandM + pos % band_rows];
   const int e = te.x;
   const int row0 = te.y;
   const int row_end = p.offsets[e + 1];
@@ -442,60 +469,87 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   const uint8_t* wexp = p.w + (size_t)e * p.w_stride;
 
   // ---- DMA sources: unit id = q * 256 + tid lands at stage byte id * 16 = LDS row id / SLOTS,
-  //      physical slot id % SLOTS, and must carry logical chunk slot ^ f(row)
-  const uint8_t* src[LOADS];
+  //      physical slot id % SLOTS, and must carry logical chunk slot ^ f(row). Units q < QW are
+  //      weight rows, the rest routed rows; 32-bit offsets from the two (uniform) bases.
+  constexpr int QW = BN * SLOTS / 256;
+  uint32_t src[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
     const int id = q * 256 + tid;
     const int row = id / SLOTS;
     const int c = (id % SLOTS) ^ big_swz<RB>(row);
-    const uint8_t* base;
-    if (row < BN) {
-      base = wexp + (size_t)(n0 + row) * ldk;
+    const uint32_t cb = 16 * c;
+    if (q < QW) {
+      src[q] = (uint32_t)((n0 + row) * ldk) + cb;
     } else {
       int r = row0 + row - BN;
       r = r < row_end ? r : row_end - 1;  // rows past the expert's end are never stored
-      base = p.rows + (size_t)r * ldk;
+      src[q] = (uint32_t)(r * ldk) + cb;
     }
-    if constexpr (MX) src[q] = base + (c < SLOTS / 2 ? 16 * c : 128 + 16 * (c - SLOTS / 2));
-    else src[q] = base + 16 * c;
   }
-  auto stage_off = [&](int kt) -> size_t {
-    // MX: stage kt holds steps s0 .. s0+SPS-1 of chunk kt / PER_CHUNK, i.e. K bytes
-    // [256 cc + 32 s0, + 32 SPS) and [256 cc + 128 + 32 s0, + 32 SPS)
-    if constexpr (MX) return (size_t)256 * (kt / PER_CHUNK) + 32 * SPS * (kt % PER_CHUNK);
-    else return (size_t)RB * kt;
-  };
-  auto issue = [&](int kt, int buf) {
-    const size_t off = stage_off(kt);
+  // stage j holds K bytes [RB j, RB j + RB) of every row (whole cache lines for RB = 128)
+  auto stage_off = [&](int j) -> size_t { return (size_t)RB * j; };
+  const int nk = (int)(ldk / RB);
+  const int nchunks = MX ? nk / PC : 0;
+  auto issue = [&](int j) {
+    const uint32_t off = (uint32_t)stage_off(j);
+    uint8_t* b = lds + (j % NS) * STAGE + wave * 1024;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q)
-      dma16(src[q] + off, lds + buf * STAGE + q * 4096 + wave * 1024);
+    for (int q = 0; q < LOADS; ++q) dma16((q < QW ? wexp : p.rows) + (src[q] + off), b + q * 4096);
   };
 
-  // ---- MX scale words: one 32-bit word (scale bytes of blocks 4g .. 4g+3 of the chunk) per
-  //      fragment row and chunk
-  const uint8_t* sw_ptr[NI];
-  const uint8_t* sr_ptr[NJ];
+  // ---- MX scale words. In K order, MFMA step s of a 256-element chunk multiplies blocks 2s (its
+  //      first block, scale from lane group 0) and 2s+1 (second block, lane group 1), so lane group
+  //      g needs the scale bytes of blocks g, 2+g, 4+g, 6+g of the chunk: one 8-byte load of the
+  //      row's chunk scales and a byte permute give that word, and the MFMA's byte select picks
+  //      step s. 32-bit offsets from the expert's and the rows' scale bases.
+  uint32_t sw_off[NI], sr_off[NJ];
   int scw[NI], scr[NJ], nscw[NI], nscr[NJ];
+  const uint8_t* wsb = MX ? p.w_scales + (size_t)e * p.ws_stride : nullptr;
+  const uint32_t perm_sel = g ? 0x07050301u : 0x06040200u;  // bytes g, 2+g of lo, g, 2+g of hi
   if constexpr (MX) {
-    const size_t nsb = (size_t)p.K / kMxBlock;
+    const uint32_t nsb = (uint32_t)(p.K / kMxBlock);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      sw_ptr[i] = p.w_scales + (size_t)e * p.ws_stride +
-                  (size_t)(n0 + 128 * wn + 32 * i + li) * nsb + 4 * g;
+    for (int i = 0; i < NI; ++i) sw_off[i] = (uint32_t)(n0 + 128 * wn + 32 * i + li) * nsb;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int r = row0 + (BM / 2) * wm + 32 * j + li;
       r = r < row_end ? r : row_end - 1;
-      sr_ptr[j] = p.row_scales + (size_t)r * nsb + 4 * g;
+      sr_off[j] = (uint32_t)r * nsb;
     }
   }
+  auto scale_word = [&](const uint8_t* base, uint32_t off, int cc) -> int {
+    const uint2 v = *reinterpret_cast<const uint2*>(base + (off + 8 * cc));
+    return (int)__builtin_amdgcn_perm(v.y, v.x, perm_sel);
+  };
   auto sload = [&](int cc, int (&w)[NI], int (&r)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) w[i] = *reinterpret_cast<const int*>(sw_ptr[i] + 8 * cc);
+    for (int i = 0; i < NI; ++i) w[i] = scale_word(wsb, sw_off[i], cc);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) r[j] = *reinterpret_cast<const int*>(sr_ptr[j] + 8 * cc);
+    for (int j = 0; j < NJ; ++j) r[j] = scale_word(p.row_scales, sr_off[j], cc);
+  };
+
+  // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact):
+  //   prologue: S(0), G(0) .. G(NS-2); barrier point j = 0 .. nk-1: wait for G(j), barrier,
+  //   G(j+NS-1) if it exists, then S(cc+1) when j = cc * PC + 1 and chunk cc+1 exists.
+  // When point j waits, the groups issued after G(j) are G(j+1 .. min(j+NS-2, nk-1)); waiting
+  // for vmcnt(LOADS * that many) completes G(j). Scale loads issued after G(j) are not counted,
+  // which only makes the wait stricter (they complete too), never too weak.
+  auto wait_stage = [&](int j) {
+    const int ng = min(j + NS - 2, nk - 1) - j;
+    asm volatile("" ::: "memory");
+    if (ng >= 3 && NS >= 5) wait_vmcnt<LOADS * (NS >= 5 ? 3 : 0)>();
+    else if (ng >= 2 && NS >= 4) wait_vmcnt<LOADS * (NS >= 4 ? 2 : 0)>();
+    else if (ng >= 1 && NS >= 3) wait_vmcnt<LOADS * (NS >= 3 ? 1 : 0)>();
+    else wait_vmcnt<0>();
+  };
+  auto barrier_point = [&](int j) {
+    wait_stage(j);
+    lds_barrier();
+    if (j + NS - 1 < nk) issue(j + NS - 1);
+    if constexpr (MX) {
+      if (j % PC == 1 && j / PC + 1 < nchunks) sload(j / PC + 1, nscw, nscr);
+    }
   };
 
   // ---- fragment byte offsets inside a stage: row * RB + 16 * (c ^ f(row)) == fb ^ (16 c)
@@ -511,6 +565,36 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     fbr[j] = row * RB + 16 * big_swz<RB>(row);
   }
 
+  using FragT = typename std::conditional<MX, i32x8_t, bf16x8_t>::type;
+  struct Frags {
+    FragT w[NI];
+    FragT r[NJ];
+  };
+  constexpr int NR = (MX ? 2 : 1) * (NI + NJ);  // 16-byte LDS reads per k-step
+  // 16-byte piece `idx` (0 .. NR-1) of the fragments of k-step t from stage buffer b; weight
+  // fragments first, each MX fragment being two pieces (its two half blocks)
+  auto load_piece = [&](Frags& F, const uint8_t* b, int t, int idx) {
+    if constexpr (!MX) {
+      const int c = 16 * (2 * t + g);
+      if (idx < NI) F.w[idx] = *reinterpret_cast<const bf16x8_t*>(b + (fbw[idx] ^ c));
+      else F.r[idx - NI] = *reinterpret_cast<const bf16x8_t*>(b + (fbr[idx - NI] ^ c));
+    } else {
+      // MFMA step t of the stage: bytes 0-15 of lane (i, g) are K [64t + 16g, +16) (first block),
+      // bytes 16-31 are K [64t + 32 + 16g, +16) (second block)
+      const int f = idx >> 1, half = idx & 1;
+      const int c = 16 * (4 * t + 2 * half + g);
+      const int fb = f < NI ? fbw[f] : fbr[f - NI];
+      const i32x4_t v = *reinterpret_cast<const i32x4_t*>(b + (fb ^ c));
+      FragT& dst = f < NI ? F.w[f] : F.r[f - NI];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[4 * half + q] = v[q];
+    }
+  };
+  auto load_frags = [&](Frags& F, const uint8_t* b, int t) {
+#pragma unroll
+    for (int idx = 0; idx < NR; ++idx) load_piece(F, b, t, idx);
+  };
+
   f32x16_t acc[NI][NJ];
 #pragma unroll
   for (int i = 0; i < NI; ++i)
@@ -519,101 +603,149 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // MFMAs of one stage; S0 = the MX chunk step of the stage's first k-step
-  auto compute = [&](const uint8_t* b, auto s0_tag) {
-    constexpr int S0 = decltype(s0_tag)::value;
+  constexpr int NM = NI * NJ;  // MFMAs per k-step
+  auto mfma_k = [&](const Frags& F, int k, int sel) {
+    const int i = k / NJ, j = k % NJ;
+    if constexpr (MX) acc[i][j] = mfma_mx_sel(sel, F.w[i], F.r[j], acc[i][j], scw[i], scr[j]);
+    else acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[i], F.r[j], acc[i][j], 0, 0, 0);
+  };
+  auto mfmas = [&](const Frags& F, int sel) {
 #pragma unroll
-    for (int t = 0; t < SPS; ++t) {
-      if constexpr (!MX) {
-        bf16x8_t wf[NI], rf[NJ];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-          wf[i] = *reinterpret_cast<const bf16x8_t*>(b + (fbw[i] ^ (16 * (2 * t + g))));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          rf[j] = *reinterpret_cast<const bf16x8_t*>(b + (fbr[j] ^ (16 * (2 * t + g))));
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], rf[j], acc[i][j], 0, 0, 0);
-      } else {
-        i32x8_t wf[NI], rf[NJ];
-        const int c0 = 16 * (2 * t + g), c1 = 16 * (SLOTS / 2 + 2 * t + g);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const i32x4_t a0 = *reinterpret_cast<const i32x4_t*>(b + (fbw[i] ^ c0));
-          const i32x4_t a1 = *reinterpret_cast<const i32x4_t*>(b + (fbw[i] ^ c1));
-          wf[i] = (i32x8_t){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const i32x4_t b0 = *reinterpret_cast<const i32x4_t*>(b + (fbr[j] ^ c0));
-          const i32x4_t b1 = *reinterpret_cast<const i32x4_t*>(b + (fbr[j] ^ c1));
-          rf[j] = (i32x8_t){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        }
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = mfma_mx_sel(S0 + t, wf[i], rf[j], acc[i][j], scw[i], scr[j]);
-      }
-    }
+    for (int k = 0; k < NM; ++k) mfma_k(F, k, sel);
   };
 
-  const int nk = (int)(ldk / RB);
-  const int nchunks = MX ? nk / PER_CHUNK : 0;
+  // ---- prologue
+  Frags FA, FB;
   if constexpr (MX) sload(0, scw, scr);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
+    if (s < nk) issue(s);
+  barrier_point(0);
+  load_frags(FA, lds, 0);
 
-  // one stage at position P of its MX chunk (P = 0 for BF16)
-  auto step = [&](int kt, auto p_tag) {
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // ---- steady-state k-step (stage j with j + NS < nk, so every wait and load is unconditional):
+  // its MFMAs interleaved one by one with the other work, in a fixed order the compiler may not
+  // change (sched_barrier): the next k-step's LDS reads, and in a stage's last k-step, right
+  // after the first MFMA, the barrier point of stage j+1 followed by the DMA of stage j+NS, the
+  // next chunk's MX scale words and the reads of stage j+1's first fragments.
+  auto kstep_fast = [&](int j, auto t_tag, auto p_tag, Frags& cur, Frags& nxt) {
+    constexpr int t = decltype(t_tag)::value;
     constexpr int P = decltype(p_tag)::value;
-    const int cc = MX ? kt / PER_CHUNK : 0;
-    // wait until this wave's loads of stage kt have landed: at most the loads issued after them
-    // may be outstanding, i.e. the next NS - 2 stages and, at chunk positions 1 .. NS - 2, the
-    // next chunk's scale words (issued at position 0, after that stage's wait). Near the end
-    // fewer loads follow, and vmcnt(0) is used.
-    if (kt + NS - 2 < nk) {
-      if constexpr (MX && P >= 1 && P <= NS - 2) {
-        if (cc + 1 < nchunks) wait_vmcnt_fenced<LOADS * (NS - 2) + NSC>();
-        else wait_vmcnt_fenced<LOADS * (NS - 2)>();
-      } else {
-        wait_vmcnt_fenced<LOADS * (NS - 2)>();
+    constexpr bool LAST = t + 1 == SPS;
+    constexpr bool SCALES = MX && LAST && P == 0;  // barrier point j+1 = cc * PC + 1
+    constexpr int NDMA = LAST ? LOADS : 0;
+    constexpr int NSCL = SCALES ? NSC : 0;
+    constexpr int NOPS = NDMA + NSCL + NR;
+    constexpr int SLOTS_M = NM - 2;  // leave the last two MFMAs to cover the last reads
+    constexpr int K = (NOPS + SLOTS_M - 1) / SLOTS_M;
+    const uint8_t* rb = LAST ? lds + ((j + 1) % NS) * STAGE : lds + (j % NS) * STAGE;
+    const int rt = LAST ? 0 : t + 1;
+    const uint32_t doff = (uint32_t)stage_off(j + NS);
+    uint8_t* db = lds + (j % NS) * STAGE + wave * 1024;  // stage j's buffer, read completely
+    const int cc_next = min(j / PC + 1, nchunks - 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      mfma_k(cur, m, P * SPS + t);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LAST) {
+        if (m == 0) {
+          wait_vmcnt_fenced<LOADS * (NS - 2)>();
+          lds_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+#pragma unroll
+      for (int o = 0; o < K; ++o) {
+        const int op = (m - 1) * K + o;
+        if (m >= 1 && op < NOPS) {
+          if (op < NDMA) {
+            dma16((op < QW ? wexp : p.rows) + (src[op] + doff), db + op * 4096);
+          } else if (op < NDMA + NSCL) {
+            const int k = op - NDMA;
+            if constexpr (MX) {
+              if (k < NI) nscw[k] = scale_word(wsb, sw_off[k], cc_next);
+              else nscr[k - NI] = scale_word(p.row_scales, sr_off[k - NI], cc_next);
+            }
+          } else {
+            load_piece(nxt, rb, rt, op - NDMA - NSCL);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- generic k-step for the last stages (conditional waits and loads)
+  auto kstep = [&](int j, auto t_tag, auto p_tag, Frags& cur, Frags& nxt) {
+    constexpr int t = decltype(t_tag)::value;
+    constexpr int P = decltype(p_tag)::value;
+    if constexpr (t + 1 < SPS) {
+      load_frags(nxt, lds + (j % NS) * STAGE, t + 1);
     } else {
-      wait_vmcnt_fenced<0>();
+      if (j + 1 < nk) {
+        barrier_point(j + 1);
+        load_frags(nxt, lds + ((j + 1) % NS) * STAGE, 0);
+      }
     }
-    lds_barrier();
-    if constexpr (MX) {
-      if (P == 0 && cc + 1 < nchunks) sload(cc + 1, nscw, nscr);
+    mfmas(cur, P * SPS + t);
+  };
+
+  // one stage; with an even number of k-steps it starts and ends on F0
+  auto stage = [&](int j, auto p_tag, auto fast_tag, Frags& F0, Frags& F1) {
+    constexpr int P = decltype(p_tag)::value;
+    constexpr bool FAST = decltype(fast_tag)::value;
+    auto ks = [&](auto t_tag, Frags& c, Frags& n) {
+      if constexpr (FAST) kstep_fast(j, t_tag, p_tag, c, n);
+      else kstep(j, t_tag, p_tag, c, n);
+    };
+    ks(I0{}, F0, F1);
+    if constexpr (SPS >= 2) ks(I1{}, F1, F0);
+    if constexpr (SPS >= 4) {
+      ks(I2{}, F0, F1);
+      ks(I3{}, F1, F0);
     }
-    if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-    compute(lds + (kt % NS) * STAGE, std::integral_constant<int, P * SPS>{});
     if constexpr (MX) {
-      if (P == PER_CHUNK - 1) {
+      if constexpr (P == PC - 1) {  // the next stage starts a new chunk
 #pragma unroll
         for (int i = 0; i < NI; ++i) scw[i] = nscw[i];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) scr[j] = nscr[j];
+        for (int q = 0; q < NJ; ++q) scr[q] = nscr[q];
       }
     }
   };
-  if constexpr (MX) {
-    static_assert(PER_CHUNK == 2 || PER_CHUNK == 4, "chunk split");
-    for (int kt = 0; kt < nk; kt += PER_CHUNK) {
-      step(kt + 0, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
-      if constexpr (PER_CHUNK == 4) {
-        step(kt + 2, std::integral_constant<int, 2>{});
-        step(kt + 3, std::integral_constant<int, 3>{});
+  // stages [j0, j1) in blocks of PC (MX) or one by one (BF16)
+  auto run = [&](int j0, int j1, auto fast_tag) {
+    if constexpr (MX) {
+      for (int j = j0; j < j1; j += PC) {
+        if constexpr (SPS == 1) {  // one k-step per stage: the fragment set alternates per stage
+          stage(j + 0, I0{}, fast_tag, FA, FB);
+          stage(j + 1, I1{}, fast_tag, FB, FA);
+          if constexpr (PC == 4) {
+            stage(j + 2, I2{}, fast_tag, FA, FB);
+            stage(j + 3, I3{}, fast_tag, FB, FA);
+          }
+        } else {
+          stage(j + 0, I0{}, fast_tag, FA, FB);
+          stage(j + 1, I1{}, fast_tag, FA, FB);
+          if constexpr (PC == 4) {
+            stage(j + 2, I2{}, fast_tag, FA, FB);
+            stage(j + 3, I3{}, fast_tag, FA, FB);
+          }
+        }
       }
+    } else {
+      for (int j = j0; j < j1; ++j) stage(j, I0{}, fast_tag, FA, FB);
     }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) step(kt, std::integral_constant<int, 0>{});
-  }
+  };
+  // steady state: stages j with j + NS < nk (rounded down to whole MX chunks), then the rest
+  const int jsteady = max(0, (nk - NS) / PC * PC);
+  run(0, jsteady, std::true_type{});
+  run(jsteady, nk, std::false_type{});
 
   // ---- epilogue. acc[i][j][q]: weight row n0 + 128 wn + 32 i + 8 (q / 4) + 4 g + q % 4,
   //      routed row row0 + (BM/2) wm + 32 j + li
@@ -804,15 +936,16 @@ struct FfnLayout {
 
 // rows per M tile: the large-tile kernel (h % 256 == 0, m % 128 == 0) takes 256 rows when the
 // experts hold 224 rows or more on average, else 128; the small-tile kernel always 128
-int ffn_tile_rows(int R, int h, int m, int E_loc) {
+int ffn_tile_rows(int R, int h, int m, int E_loc, bool mx) {
   if (h % kBigBN || (2 * m) % kBigBN) return kBM;
+  if (mx) return 128;  // the 256-row MXFP8 tile does not fit the register file
   return (R / E_loc >= 224) ? 256 : 128;
 }
 bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 
 FfnLayout ffn_layout(int R, int h, int m, int E_loc, bool mx) {
   FfnLayout L{};
-  const int bm = ffn_tile_rows(R, h, m, E_loc);
+  const int bm = ffn_tile_rows(R, h, m, E_loc, mx);
   L.max_tiles = (R + bm - 1) / bm + E_loc;
   size_t off = 0;
   L.count = off;
@@ -875,7 +1008,7 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
                              int m, int E_loc, bool mx, hipStream_t st, const hipEvent_t* ev) {
   const PreparedLayout P = prepared_layout(E_loc, h, m, mx);
   const FfnLayout F = ffn_layout(R, h, m, E_loc, mx);
-  const int bm = ffn_tile_rows(R, h, m, E_loc);
+  const int bm = ffn_tile_rows(R, h, m, E_loc, mx);
   const bool big = ffn_big(h, m);
   const uint8_t* pw = reinterpret_cast<const uint8_t*>(prepared);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
@@ -918,21 +1051,30 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
 
   if (big) {
     // the XCD remap needs the grid rounded up to a multiple of 8
-    const dim3 g1((F.max_tiles * ((2 * m) / kBigBN) + 7) / 8 * 8);
-    const dim3 g2((F.max_tiles * (h / kBigBN) + 7) / 8 * 8);
+    // per XCD at most ceil(tiles / 8) plus one per band: the grid covers 8 times that
+    auto big_grid = [&](int nt) {
+      return dim3(8 * ((F.max_tiles * nt + 7) / 8 + F.max_tiles / kBandM + 2));
+    };
+    const dim3 g1 = big_grid((2 * m) / kBigBN), g2 = big_grid(h / kBigBN);
     // kernels launched by name here so that each instantiation is compiled for the device
 #define MOE_BIG(MXV, SW, BMV, G, A)                                                             \
     hipLaunchKernelGGL((grouped_gemm_big_kernel<MXV, SW, BMV, (MXV ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16), \
-                                                (MXV ? MOE_BIG_NS_MX : MOE_BIG_NS_BF16)>),      \
+                                                (MXV ? MOE_BIG_NS_MX                            \
+                                                     : (BMV == 128 ? MOE_BIG_NS_BF16_128        \
+                                                                   : MOE_BIG_NS_BF16))>),       \
                        G, dim3(256), 0, st, A)
-    if (bm == 256) {
-      if (mx) MOE_BIG(true, true, 256, g1, a1); else MOE_BIG(false, true, 256, g1, a1);
+    if (mx) {  // MXFP8 always takes 128-row tiles
+      MOE_BIG(true, true, 128, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
-      if (mx) MOE_BIG(true, false, 256, g2, a2); else MOE_BIG(false, false, 256, g2, a2);
+      MOE_BIG(true, false, 128, g2, a2);
+    } else if (bm == 256) {
+      MOE_BIG(false, true, 256, g1, a1);
+      if (ev) (void)hipEventRecord(ev[1], st);
+      MOE_BIG(false, false, 256, g2, a2);
     } else {
-      if (mx) MOE_BIG(true, true, 128, g1, a1); else MOE_BIG(false, true, 128, g1, a1);
+      MOE_BIG(false, true, 128, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
-      if (mx) MOE_BIG(true, false, 128, g2, a2); else MOE_BIG(false, false, 128, g2, a2);
+      MOE_BIG(false, false, 128, g2, a2);
     }
 #undef MOE_BIG
     if (ev) (void)hipEventRecord(ev[2], st);
