@@ -18,6 +18,7 @@ workload's tokens on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -81,6 +82,28 @@ def stage_bytes(wl) -> dict:
         "combine": R * h * 2 + R * 8 + T * h * 2 + (T * h * 2 if wl.m_shared else 0),
         "topk": T * wl.E * 4 + R * 8 if wl.mode == "router" else 0,
     }
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCE = os.path.join(ROOT, "routing_expert_grouped_amd", "csrc", "moe_gemm_kernels.hip")
+
+
+def measured_traffic(workload: str):
+    """L2-to-fabric bytes per GEMM-1 launch from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None when there is no
+    summary or the GEMM source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src:
+        return None
+    return int(kv["gemm1_bytes_per_launch"])
 
 
 def cpu_baseline(wl, inp, weights_host, shared_host, n_tokens: int) -> dict:
@@ -223,7 +246,7 @@ def main() -> int:
                    "mode": wl.mode, "m_shared": wl.m_shared},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM-1 (gate/up + SwiGLU epilogue)",
                      "achieved": round(g1_tf, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(g1_tf / peak, 4), "traffic": None},
+                     "frac": round(g1_tf / peak, 4), "traffic": measured_traffic(wl.name)},
         "grouped_gemm_mfma_frac": round(gemm_tf / peak, 4),
         "layer_tflops": round(fl["total"] / (ms_per_step * 1e-3) / 1e12, 1),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},

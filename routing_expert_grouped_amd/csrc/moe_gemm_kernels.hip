@@ -331,13 +331,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
 // 8-lane and 16-lane LDS phases. The swizzle is applied on the global side: the DMA writes a
 // wave's 64 lanes to 1 KB of consecutive LDS, and each lane fetches the chunk for its slot.
 //
-// Work order: the M tiles are cut into bands of 8; all XCDs work on the same band at the same
-// time (so the band's rows and its experts' weights stay in the MALL), and inside a band XCD x
-// takes the x-th eighth of the band's tiles in N-major order, i.e. a block of about Nt/8 weight
-// panels by 8 row panels that its 32 CUs share through its L2. Workgroup L runs on XCD L % 8.
+// Work order: the M tiles are cut into bands of about 256 / Nt tiles; all XCDs work on the same
+// band at the same time (so the band's rows and its experts' weights stay in the MALL), and
+// inside a band XCD x takes the x-th eighth of the band's tiles in N-major order, i.e. a block of
+// about Nt/8 weight panels by band-height row panels, about the 32 tiles its CUs run at once and
+// share through its L2. Workgroup L runs on XCD L % 8.
 // ------------------------------------------------------------------------------------------------
 constexpr int kBigBN = 256;
-constexpr int kBandM = 8;
+// band height in M tiles: about 256 tiles per band, i.e. about the 32 concurrent workgroups of
+// each XCD per band share
+__host__ __device__ inline int band_rows_for(int Nt) {
+  const int b = (256 + Nt / 2) / Nt;
+  return b < 4 ? 4 : (b > 16 ? 16 : b);
+}
 
 template <int RB>
 __device__ __forceinline__ int big_swz(int row) {
@@ -427,31 +433,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   static_assert(NS * STAGE <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
 
-  // ---- which tile: band b of 8 M tiles, XCD x takes the x-th eighth of it (N-major)
+  // ---- which tile: band b of band_m M tiles, XCD x takes the x-th eighth of it (N-major)
   const int mt_total = *p.tile_count;
   const int Nt = p.N / BN;
+  const int band_m = band_rows_for(Nt);
   const int x = blockIdx.x & 7;
   int jx = blockIdx.x >> 3;  // this workgroup's index among the XCD's workgroups
-  const int nb_full = mt_total / kBandM;
-  const int tb_full = kBandM * Nt;
+  const int nb_full = mt_total / band_m;
+  const int tb_full = band_m * Nt;
   const int share_full = ((x + 1) * tb_full >> 3) - (x * tb_full >> 3);
   int band, band_rows, tb;
   if (jx < nb_full * share_full) {
     band = jx / share_full;
     jx -= band * share_full;
-    band_rows = kBandM;
+    band_rows = band_m;
     tb = tb_full;
   } else {
     jx -= nb_full * share_full;
     band = nb_full;
-    band_rows = mt_total - nb_full * kBandM;
+    band_rows = mt_total - nb_full * band_m;
     tb = band_rows * Nt;
     const int share_last = ((x + 1) * tb >> 3) - (x * tb >> 3);
     if (jx >= share_last) return;  // surplus workgroup: leaves before any barrier
   }
   const int pos = (x * tb >> 3) + jx;
   const int nt = pos / band_rows;
-  const int2 te = p.tiles[band * kBandM + pos % band_rows];
+  const int2 te = p.tiles[band * band_m + pos % band_rows];
   const int e = te.x;
   const int row0 = te.y;
   const int row_end = p.offsets[e + 1];
@@ -1053,7 +1060,7 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
     // the XCD remap needs the grid rounded up to a multiple of 8
     // per XCD at most ceil(tiles / 8) plus one per band: the grid covers 8 times that
     auto big_grid = [&](int nt) {
-      return dim3(8 * ((F.max_tiles * nt + 7) / 8 + F.max_tiles / kBandM + 2));
+      return dim3(8 * ((F.max_tiles * nt + 7) / 8 + F.max_tiles / band_rows_for(nt) + 2));
     };
     const dim3 g1 = big_grid((2 * m) / kBigBN), g2 = big_grid(h / kBigBN);
     // kernels launched by name here so that each instantiation is compiled for the device
