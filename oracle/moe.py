@@ -280,19 +280,69 @@ def dsilu(z: np.ndarray) -> np.ndarray:
     return s * (1.0 + z * (1.0 - s))
 
 
-def layer_backward(wl, inp: dict, fwd: dict, weights_of, dy_f64=None):
-    """Gradients of the expert path: dX and per-expert dW_gate, dW_up, dW_down, in float64.
+def _mx_rows(v: np.ndarray) -> np.ndarray:
+    """MX round trip along axis 0 (the routed rows of one expert): blocks of 32 rows counted from
+    the expert's first row, the last block zero-padded (Reading: the wgrad GEMMs reduce over an
+    expert's rows, so their MX blocks run along those rows)."""
+    n = v.shape[0]
+    if n == 0:
+        return v.copy()
+    pad = (-n) % 32
+    if pad:
+        v = np.concatenate([v, np.zeros((pad,) + v.shape[1:], dtype=v.dtype)], axis=0)
+    return mx_roundtrip(v, axis=0)[:n]
+
+
+def expert_backward(a: np.ndarray, dO: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                    w_down: np.ndarray, mx: bool = False):
+    """Backward of one SwiGLU expert with respect to its input rows and its three weights.
+
+    a: [n, h] the expert's routed rows before any quantisation; dO: [n, h] the gradient of its
+    output rows; w_gate, w_up: [h, m]; w_down: [m, h]. Returns (dA, dW_gate, dW_up, dW_down).
+
+    With G = a W_gate, U = a W_up (the forward's values, from its MX operands when mx) and
+    H = silu(G) * U:
+      dH = dO W_down^T;  dG = dH * U * dsilu(G);  dU = dH * silu(G)
+      dA = dG W_gate^T + dU W_up^T
+      dW_gate = a^T dG;  dW_up = a^T dU;  dW_down = H^T dO
+    With mx=True every operand of these five GEMMs is MX-quantised along that GEMM's reduction
+    axis (Reading: as in the forward, which quantises each GEMM's operands along its reduction
+    axis): dO and W_down along h for dH; dG, dU, W_gate and W_up along m for dA; a, dG, dU, H and
+    dO along the expert's rows for the weight gradients. The quantised values are those of the
+    unrounded float64 quantities (a: the bf16 input itself).
+    """
+    if mx:
+        aq, wgq, wuq = mx_roundtrip(a, axis=1), mx_roundtrip(w_gate, axis=0), \
+            mx_roundtrip(w_up, axis=0)
+    else:
+        aq, wgq, wuq = a, w_gate, w_up
+    g, u = aq @ wgq, aq @ wuq
+    hdn = silu(g) * u
+
+    def q(v, axis):
+        if not mx:
+            return v
+        return _mx_rows(v) if axis == "rows" else mx_roundtrip(v, axis=axis)
+
+    dh = q(dO, 1) @ q(w_down, 1).T
+    dg = dh * u * dsilu(g)
+    du = dh * silu(g)
+    dA = q(dg, 1) @ q(w_gate, 1).T + q(du, 1) @ q(w_up, 1).T
+    ar = q(a, "rows")
+    return dA, ar.T @ q(dg, "rows"), ar.T @ q(du, "rows"), q(hdn, "rows").T @ q(dO, "rows")
+
+
+def layer_backward(wl, inp: dict, fwd: dict, weights_of, dy_f64=None, mx=None):
+    """Gradients of the expert path: dX and per-expert (dW_gate, dW_up, dW_down), in float64.
 
     Reading: the gate weights w are held fixed (the router's own gradient is not part of the
-    expert path), so with a = perm[r] and t = a div k:
-      dO[r]     = w[a] * dY[t]
-      dH        = dO W_down^T;  dG = dH * U * dsilu(G);  dU = dH * silu(G)
-      dA        = dG W_gate^T + dU W_up^T
-      dW_gate_e = A_e^T dG_e;   dW_up_e = A_e^T dU_e;   dW_down_e = H_e^T dO_e
-      dX[t]     = sum over j ascending of dA[inv[t*k + j]]
-    (Unquantised float64; the MX variant of the backward quantises the same operands along each
-    GEMM's reduction axis.)
+    expert path), so with a = perm[r] and t = a div k the gradient of routed row r's output is
+    dO[r] = w[a] * dY[t]; each expert then runs expert_backward on its rows, and
+      dX[t] = sum over j ascending of dA[inv[t*k + j]]
+    (the un-permute). mx defaults to the workload's dtype being MXFP8.
     """
+    if mx is None:
+        mx = wl.dtype == "mxfp8"
     k = wl.k
     perm, inv, offsets = fwd["perm"], fwd["inv"], fwd["offsets"]
     dy = bf16_to_f64(inp["dy"]) if dy_f64 is None else dy_f64
@@ -305,16 +355,11 @@ def layer_backward(wl, inp: dict, fwd: dict, weights_of, dy_f64=None):
     for e in range(wl.E_loc):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         wg, wu, wd = (bf16_to_f64(v) for v in weights_of(e))
-        a = A[r0:r1]
-        g, u = a @ wg, a @ wu
-        hdn = silu(g) * u
-        dh = dO[r0:r1] @ wd.T
-        dg = dh * u * dsilu(g)
-        du = dh * silu(g)
-        dA[r0:r1] = dg @ wg.T + du @ wu.T
-        dW.append((a.T @ dg, a.T @ du, hdn.T @ dO[r0:r1]))
+        dA[r0:r1], dwg, dwu, dwd = expert_backward(A[r0:r1], dO[r0:r1], wg, wu, wd, mx=mx)
+        dW.append((dwg, dwu, dwd))
     dX = np.zeros_like(dy)
     invk = inv.astype(np.int64).reshape(-1, k)
     for j in range(k):
-        dX += dA[invk[:, j]]
+        sel = invk[:, j] >= 0
+        dX[sel] += dA[invk[sel, j]]
     return dX, dW
