@@ -21,7 +21,7 @@
  *     alone size every launch; the device-side expert counts are never read by the host.
  *   - Ownership: the caller owns every buffer, including workspaces (sized by the *_bytes
  *     queries) and prepared weights. Buffers must not overlap unless stated.
- *   - Alignment: every pointer must be 256-byte aligned (torch allocations are).
+ *   - Alignment: every pointer must be 16-byte aligned (torch allocations are 256-byte aligned).
  *   - Errors: arguments are checked on the host before anything is enqueued. MOE_EINVAL means a
  *     null required pointer, a misaligned pointer or an inconsistent shape, and nothing was
  *     enqueued. MOE_EUNSUPPORTED means a valid shape the kernels do not cover (see each call).
@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -164,14 +164,18 @@ moe_status moe_combine(const moe_shape* s, const uint16_t* out_rows, const int32
  *   weights given by the caller (one expert-parallel rank's share).
  * prepared: E_loc experts from moe_prepare_weights(dt); shared_prepared: BF16 shared expert
  *   (shape.m_shared > 0) or NULL. y [T][h] bf16 output.
+ * saved: NULL, or moe_saved_bytes() bytes that receive what moe_backward needs (training): the
+ *   schedule (offsets, perm, inv), the gate weight of every assignment and GEMM-1's G and U in
+ *   float32. Needs h % 256 == 0 and m % 256 == 0 (else MOE_EUNSUPPORTED).
  * ws: moe_forward_workspace_bytes() bytes. The intermediates stay in it; moe_forward_views()
  *   gives their addresses.
  * ------------------------------------------------------------------------------------------- */
 size_t moe_forward_workspace_bytes(const moe_shape* s, moe_dtype dt);
+size_t moe_saved_bytes(const moe_shape* s, moe_dtype dt);
 moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                        const uint16_t* w_router, const float* bias, const int32_t* assign,
                        const float* assign_w, const void* prepared, const void* shared_prepared,
-                       uint16_t* y, void* ws, void* stream);
+                       uint16_t* y, void* saved, void* ws, void* stream);
 
 /* Profiling variant of moe_forward: the same work on the same stream, plus hipEventRecord of the
  * caller's events at the stage boundaries, so a caller can time each kernel live:
@@ -184,7 +188,8 @@ moe_status moe_forward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t
                                 const uint16_t* w_router, const float* bias,
                                 const int32_t* assign, const float* assign_w,
                                 const void* prepared, const void* shared_prepared, uint16_t* y,
-                                void* ws, void* const* events /* host */, void* stream);
+                                void* saved, void* ws, void* const* events /* host */,
+                                void* stream);
 
 /* Addresses of the intermediates moe_forward leaves in `ws` (device pointers into ws; NULL when a
  * buffer does not exist for this shape). Host-only arithmetic, nothing is enqueued. */
@@ -203,6 +208,49 @@ typedef struct {
 } moe_forward_views_t;
 moe_status moe_forward_views(const moe_shape* s, moe_dtype dt, void* ws,
                              moe_forward_views_t* views /* host */);
+
+/* ---------------------------------------------------------------------------------------------
+ * Backward of the expert path (the page's Key claims measure the MXFP8 backward with the same
+ * fused quantisation as the forward; its flowchart mirrors dispatch and combine backwards).
+ * The gate weights are held fixed (the router's own gradient is not computed). With a = perm[r],
+ * t = a / k and the forward's G, U, H = silu(G) * U of routed row r:
+ *   dO[r] = w[a] dY[t];  dH = dO W_down^T;  dG = dH * U * silu'(G);  dU = dH * silu(G)
+ *   dA = dG W_gate^T + dU W_up^T;   dX[t] = sum over j = 0 .. k-1 ascending of dA[inv[t*k+j]]
+ *   dW_gate[e] = A_e^T dG_e;  dW_up[e] = A_e^T dU_e;  dW_down[e] = H_e^T dO_e
+ * where A_e, dG_e, ... are expert e's routed rows. MOE_MXFP8 quantises every operand of these
+ * GEMMs per 32 along that GEMM's reduction axis: dO, W_down along h; dG, dU, W_gate, W_up along
+ * m; A, dG, dU, H, dO along the expert's rows (blocks from its first row, zero-padded). dO, dG,
+ * dU and H are quantised from their float32 values (G and U are kept in float32 by the forward),
+ * the A rows from the bf16 input. MOE_BF16 rounds dO, dG, dU and H to bf16 instead. Accumulation
+ * is float32 everywhere, with no atomics and a fixed order.
+ *
+ * moe_prepare_bwd_weights: the backward's weight layout (offline), from the same bf16 weights as
+ *   moe_prepare_weights: W_down rows [e][m][h] (K = h) and [W_gate | W_up] rows [e][h][2m]
+ *   interleaved per 32 (K = 2m), MX-quantised along K for MOE_MXFP8.
+ * moe_backward: x [T][h] bf16 (the forward's input), dy [T][h] bf16, saved from moe_forward with
+ *   the same shape and dtype, prepared_bwd from moe_prepare_bwd_weights. Outputs dx [T][h] bf16,
+ *   dw_gate and dw_up [E_loc][h][m], dw_down [E_loc][m][h], float32 when dw_fp32 = 1, bf16 when 0
+ *   (every element is written; an expert with no rows gets zeros).
+ * Shapes: h % 256 == 0 and m % 256 == 0, else MOE_EUNSUPPORTED. ws: moe_backward_workspace_bytes().
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_prepared_bwd_weight_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_prepare_bwd_weights(const moe_shape* s, moe_dtype dt, const uint16_t* w_gate,
+                                   const uint16_t* w_up, const uint16_t* w_down,
+                                   void* prepared_bwd, void* stream);
+size_t moe_backward_workspace_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_backward(const moe_shape* s, moe_dtype dt, const uint16_t* x, const uint16_t* dy,
+                        const void* saved, const void* prepared_bwd, uint16_t* dx, void* dw_gate,
+                        void* dw_up, void* dw_down, int dw_fp32, void* ws, void* stream);
+
+/* Profiling variant of moe_backward, events recorded at its stage boundaries:
+ *   ev[0] tables ev[1] un-combine ev[2] dH + SwiGLU backward ev[3] dA ev[4] un-permute ev[5]
+ *   transposes ev[6] dW_gate | dW_up ev[7] dW_down ev[8] */
+#define MOE_BWD_PROFILE_EVENTS 9
+moe_status moe_backward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                 const uint16_t* dy, const void* saved, const void* prepared_bwd,
+                                 uint16_t* dx, void* dw_gate, void* dw_up, void* dw_down,
+                                 int dw_fp32, void* ws, void* const* events /* host */,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,15 +15,17 @@ from typing import Optional
 
 import torch
 
-from ._lib import (MOE_BF16, MOE_MXFP8, MOE_PROFILE_EVENTS, STAGES, MoeError, MoeForwardViews,
-                   MoeShape, check, load)
+from ._lib import (BWD_STAGES, MOE_BF16, MOE_BWD_PROFILE_EVENTS, MOE_MXFP8, MOE_PROFILE_EVENTS,
+                   STAGES, MoeError, MoeForwardViews, MoeShape, check, load)
 
 __all__ = [
     "MOE_BF16", "MOE_MXFP8", "MoeError", "make_shape", "dtype_code",
     "moe_prepared_weight_bytes", "moe_prepare_weights", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
-    "HipEvents", "STAGES",
+    "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
+    "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
+    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_profiled",
 ]
 
 
@@ -172,9 +174,10 @@ def moe_forward_workspace_bytes(shape: MoeShape, dtype) -> int:
 
 
 def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, assign=None,
-                assign_w=None, shared_prepared=None, y=None, ws=None, stream=None):
+                assign_w=None, shared_prepared=None, y=None, ws=None, saved=None, stream=None):
     """The whole layer. Returns (y, ws); moe_forward_views(shape, dtype, ws) exposes the
-    intermediates left in ws."""
+    intermediates left in ws. saved: a moe_saved_bytes() uint8 tensor that receives what
+    moe_backward needs, or None."""
     dt = dtype_code(dtype)
     T, h, k = shape.T, shape.h, shape.k
     dev = _dev(x)
@@ -188,14 +191,16 @@ def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, a
         _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
         _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
         _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
-        _ptr(ws, "ws"), _stream(stream)))
+        _ptr(saved, "saved", torch.uint8), _ptr(ws, "ws"), _stream(stream)))
     return y, ws
 
 
 class HipEvents:
-    """MOE_PROFILE_EVENTS timing events from the HIP runtime (hipEventCreate / ElapsedTime)."""
+    """Timing events from the HIP runtime (hipEventCreate / ElapsedTime), one per stage boundary
+    of a profiled forward (default) or backward (names=BWD_STAGES)."""
 
-    def __init__(self, n: int = MOE_PROFILE_EVENTS):
+    def __init__(self, n: int = MOE_PROFILE_EVENTS, names=None):
+        self.names = list(STAGES if names is None else names)
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -221,7 +226,7 @@ class HipEvents:
 
     def stage_ms(self) -> dict:
         """Milliseconds of each stage of the last profiled forward."""
-        return {name: self.elapsed_ms(i, i + 1) for i, name in enumerate(STAGES)}
+        return {name: self.elapsed_ms(i, i + 1) for i, name in enumerate(self.names)}
 
     def close(self) -> None:
         for i in range(self.n):
@@ -232,7 +237,7 @@ class HipEvents:
 
 def moe_forward_profiled(shape: MoeShape, dtype, x, prepared, events: HipEvents, w_router=None,
                          bias=None, assign=None, assign_w=None, shared_prepared=None, y=None,
-                         ws=None, stream=None):
+                         ws=None, saved=None, stream=None):
     """moe_forward plus HIP events at the stage boundaries (events.stage_ms() afterwards)."""
     dt = dtype_code(dtype)
     T, h, k = shape.T, shape.h, shape.k
@@ -245,7 +250,8 @@ def moe_forward_profiled(shape: MoeShape, dtype, x, prepared, events: HipEvents,
         _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
         _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
         _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
-        _ptr(ws, "ws"), ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
+        _ptr(saved, "saved", torch.uint8), _ptr(ws, "ws"),
+        ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
     return y, ws
 
 
@@ -281,3 +287,73 @@ def moe_forward_views(shape: MoeShape, dtype, ws) -> dict:
         "out_rows": view(v.out_rows, R * h * 2, torch.bfloat16, (R, h)),
         "shared_out": view(v.shared_out, T * h * 2, torch.bfloat16, (T, h)),
     }
+
+
+def moe_saved_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_saved_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_prepared_bwd_weight_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_prepared_bwd_weight_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_prepare_bwd_weights(shape: MoeShape, dtype, w_gate, w_up, w_down, prepared_bwd=None,
+                            stream=None):
+    dt = dtype_code(dtype)
+    n = moe_prepared_bwd_weight_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_prepared_bwd_weight_bytes", 2, "shape rejected")
+    if prepared_bwd is None:
+        prepared_bwd = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
+    e, h, m = shape.E_loc, shape.h, shape.m
+    check("moe_prepare_bwd_weights", load().moe_prepare_bwd_weights(
+        ctypes.byref(shape), dt,
+        _ptr(w_gate, "w_gate", torch.bfloat16, e * h * m),
+        _ptr(w_up, "w_up", torch.bfloat16, e * h * m),
+        _ptr(w_down, "w_down", torch.bfloat16, e * m * h),
+        _ptr(prepared_bwd, "prepared_bwd", torch.uint8, n), _stream(stream)))
+    return prepared_bwd
+
+
+def moe_backward_workspace_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_backward_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws):
+    dt = dtype_code(dtype)
+    T, h, m, E_loc = shape.T, shape.h, shape.m, shape.E_loc
+    dev = _dev(x)
+    dx = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if dx is None else dx
+    wdt = torch.float32 if dw_fp32 else torch.bfloat16
+    if dw is None:
+        dw = (torch.empty(E_loc, h, m, dtype=wdt, device=dev),
+              torch.empty(E_loc, h, m, dtype=wdt, device=dev),
+              torch.empty(E_loc, m, h, dtype=wdt, device=dev))
+    n = moe_backward_workspace_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_backward_workspace_bytes", 2, "shape rejected")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    args = [ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h),
+            _ptr(dy, "dy", torch.bfloat16, T * h), _ptr(saved, "saved", torch.uint8),
+            _ptr(prepared_bwd, "prepared_bwd", torch.uint8), _ptr(dx, "dx", torch.bfloat16, T * h),
+            _ptr(dw[0], "dw_gate", wdt, E_loc * h * m), _ptr(dw[1], "dw_up", wdt, E_loc * h * m),
+            _ptr(dw[2], "dw_down", wdt, E_loc * m * h), 1 if dw_fp32 else 0, _ptr(ws, "ws")]
+    return args, dx, dw, ws
+
+
+def moe_backward(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, dx=None, dw=None,
+                 dw_fp32: bool = True, ws=None, stream=None):
+    """Backward of the expert path. Returns (dx, (dw_gate, dw_up, dw_down), ws)."""
+    args, dx, dw, ws = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws)
+    check("moe_backward", load().moe_backward(*args, _stream(stream)))
+    return dx, dw, ws
+
+
+def moe_backward_profiled(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, events: HipEvents,
+                          dx=None, dw=None, dw_fp32: bool = True, ws=None, stream=None):
+    """moe_backward plus HIP events at its stage boundaries (events.stage_ms() afterwards; create
+    the events with HipEvents(MOE_BWD_PROFILE_EVENTS, BWD_STAGES))."""
+    args, dx, dw, ws = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws)
+    check("moe_backward_profiled", load().moe_backward_profiled(
+        *args, ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
+    return dx, dw, ws

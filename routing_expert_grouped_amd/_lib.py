@@ -23,11 +23,16 @@ EXPORTS = [
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
     "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
+    "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
+    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_profiled",
 ]
 
 MOE_PROFILE_EVENTS = 10
 STAGES = ["router_logits", "topk", "schedule", "gather", "tile_table", "gemm1_gate_up_swiglu",
           "gemm2_down", "shared_expert", "combine"]
+MOE_BWD_PROFILE_EVENTS = 9
+BWD_STAGES = ["tables", "uncombine", "dgrad_dh_dswiglu", "dgrad_da", "unpermute", "transposes",
+              "wgrad_gate_up", "wgrad_down"]
 
 
 class MoeShape(ctypes.Structure):
@@ -74,9 +79,15 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (I, [S, I, P, P, P, P, P, P, P]),
         "moe_combine": (I, [S, P, P, P, P, P, P]),
         "moe_forward_workspace_bytes": (Z, [S, I]),
-        "moe_forward": (I, [S, I, P, P, P, P, P, P, P, P, P, P]),
-        "moe_forward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P]),
+        "moe_forward": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P]),
+        "moe_forward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P, P]),
         "moe_forward_views": (I, [S, I, P, ctypes.POINTER(MoeForwardViews)]),
+        "moe_saved_bytes": (Z, [S, I]),
+        "moe_prepared_bwd_weight_bytes": (Z, [S, I]),
+        "moe_prepare_bwd_weights": (I, [S, I, P, P, P, P, P]),
+        "moe_backward_workspace_bytes": (Z, [S, I]),
+        "moe_backward": (I, [S, I, P, P, P, P, P, P, P, P, I, P, P]),
+        "moe_backward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, I, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

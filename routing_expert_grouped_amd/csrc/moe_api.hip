@@ -1,5 +1,7 @@
 // C-ABI front end: argument checks, workspace layout and the launch sequence of each entry point.
 // Nothing here allocates or synchronises; every call only enqueues kernels on the caller's stream.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -30,7 +32,88 @@ moe_status check_expert_shape(const moe_shape* s, moe_dtype dt) {
   if (s->m % 64) return MOE_EUNSUPPORTED;
   if (dt == MOE_MXFP8 && (s->h % 256 || s->m % 256)) return MOE_EUNSUPPORTED;
   if (s->m_shared && s->m_shared % 64) return MOE_EUNSUPPORTED;
+  // the grouped GEMMs address rows with 32-bit byte offsets
+  const size_t el = dt == MOE_MXFP8 ? 1 : 2;
+  if ((size_t)s->T * s->k * (size_t)std::max(s->h, 2 * s->m) * el >= (1ull << 32))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
+}
+
+// Shapes the backward (and a forward that saves for it) covers.
+moe_status check_backward_shape(const moe_shape* s, moe_dtype dt) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (s->h % 256 || s->m % 256) return MOE_EUNSUPPORTED;
+  const size_t el = dt == MOE_MXFP8 ? 1 : 2;
+  const size_t kg = (size_t)wgrad_k_align(dt == MOE_MXFP8);
+  const size_t kmax = ((size_t)s->T * s->k + (size_t)s->E_loc * (kg - 1)) / kg * kg;
+  if (kmax >= (1ull << 31)) return MOE_EUNSUPPORTED;
+  if ((size_t)std::max(s->h, 2 * s->m) * kmax * el >= (1ull << 32)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Saved activations of a training forward (moe_saved_bytes).
+struct SavedLayout {
+  size_t offsets, perm, inv, w, gu, total;
+};
+
+SavedLayout saved_layout(const moe_shape* s) {
+  SavedLayout L{};
+  const size_t R = (size_t)s->T * s->k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.offsets = take((size_t)(s->E_loc + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.w = take(R * 4);
+  L.gu = take(R * 2 * s->m * 4);  // float32
+  L.total = off;
+  return L;
+}
+
+// Workspace of the backward (moe_backward_workspace_bytes).
+struct BackwardLayout {
+  size_t tiles, koff, dO, dO_s, dgu, dgu_s, dgu_f32, dA, At, At_s, dOt, dOt_s, Ht, Ht_s, dGUt,
+      dGUt_s, total;
+  int kmax;
+};
+
+BackwardLayout backward_layout(const moe_shape* s, moe_dtype dt) {
+  BackwardLayout L{};
+  const bool mx = dt == MOE_MXFP8;
+  const size_t el = mx ? 1 : 2;
+  const int R = s->T * s->k, h = s->h, m = s->m;
+  const int kg = wgrad_k_align(mx);
+  L.kmax = (int)(((size_t)R + (size_t)s->E_loc * (kg - 1)) / kg * kg);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.tiles = take(gemm_tiles_bytes(R, s->E_loc));
+  L.koff = take((size_t)(s->E_loc + 1) * 4);
+  L.dO = take((size_t)R * h * el);
+  L.dO_s = mx ? take((size_t)R * (h / kMxBlock)) : 0;
+  L.dgu = take((size_t)R * 2 * m * el);
+  L.dgu_s = mx ? take((size_t)R * (2 * m / kMxBlock)) : 0;
+  L.dgu_f32 = take((size_t)R * 2 * m * 4);
+  L.dA = take((size_t)R * h * 2);
+  const size_t km = (size_t)L.kmax;
+  L.At = take(h * km * el);
+  L.At_s = mx ? take(h * km / kMxBlock) : 0;
+  L.dOt = take(h * km * el);
+  L.dOt_s = mx ? take(h * km / kMxBlock) : 0;
+  L.Ht = take(m * km * el);
+  L.Ht_s = mx ? take(m * km / kMxBlock) : 0;
+  L.dGUt = take(2 * m * km * el);
+  L.dGUt_s = mx ? take(2 * m * km / kMxBlock) : 0;
+  L.total = off;
+  return L;
 }
 
 moe_status check_router_shape(const moe_shape* s) {
@@ -223,9 +306,14 @@ namespace {
 moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                         const uint16_t* w_router, const float* bias, const int32_t* assign,
                         const float* assign_w, const void* prepared, const void* shared_prepared,
-                        uint16_t* y, void* ws, const hipEvent_t* ev, void* stream) {
+                        uint16_t* y, void* saved, void* ws, const hipEvent_t* ev, void* stream) {
   moe_status st = check_expert_shape(s, dt);
   if (st != MOE_OK) return st;
+  if (saved) {
+    if (!ok_ptr(saved)) return MOE_EINVAL;
+    st = check_backward_shape(s, dt);
+    if (st != MOE_OK) return st;
+  }
   const bool router = w_router != nullptr;
   if (router) {
     st = check_router_shape(s);
@@ -280,9 +368,12 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
   }
   mark(4);
   uint16_t* out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
+  uint8_t* sv = reinterpret_cast<uint8_t*>(saved);
+  const SavedLayout SL = saved_layout(s);
   if (e == hipSuccess)
     e = launch_expert_ffn(b + L.rows, mx ? b + L.row_scales : nullptr, offsets, prepared, out_rows,
-                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs, ev ? ev + 5 : nullptr);
+                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs, ev ? ev + 5 : nullptr,
+                          sv ? reinterpret_cast<float*>(sv + SL.gu) : nullptr);
   uint16_t* shared_out = nullptr;
   if (e == hipSuccess && s->m_shared > 0) {
     int32_t* soff = reinterpret_cast<int32_t*>(b + L.shared_off);
@@ -296,6 +387,86 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
   mark(8);
   if (e == hipSuccess) e = launch_combine(out_rows, inv, a_w, shared_out, y, T, h, k, hs);
   mark(9);
+  if (sv && e == hipSuccess) {  // what the backward needs besides G and U (a few bytes per row)
+    e = hipMemcpyAsync(sv + SL.offsets, offsets, (size_t)(s->E_loc + 1) * 4,
+                       hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sv + SL.perm, perm, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sv + SL.inv, inv, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sv + SL.w, a_w, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
+  }
+  return hip_status(e);
+}
+
+moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, const uint16_t* dy,
+                         const void* saved, const void* prepared_bwd, uint16_t* dx, void* dw_gate,
+                         void* dw_up, void* dw_down, int dw_fp32, void* ws, const hipEvent_t* ev,
+                         void* stream) {
+  const moe_status st = check_backward_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(x) || !ok_ptr(dy) || !ok_ptr(saved) || !ok_ptr(prepared_bwd) || !ok_ptr(dx) ||
+      !ok_ptr(dw_gate) || !ok_ptr(dw_up) || !ok_ptr(dw_down) || !ok_ptr(ws))
+    return MOE_EINVAL;
+  if (dw_fp32 != 0 && dw_fp32 != 1) return MOE_EINVAL;
+  const bool mx = dt == MOE_MXFP8;
+  const int T = s->T, h = s->h, m = s->m, k = s->k, E_loc = s->E_loc, R = T * k;
+  const hipStream_t hs = as_stream(stream);
+  const SavedLayout SL = saved_layout(s);
+  const BackwardLayout L = backward_layout(s, dt);
+  const uint8_t* sv = reinterpret_cast<const uint8_t*>(saved);
+  const int32_t* offsets = reinterpret_cast<const int32_t*>(sv + SL.offsets);
+  const int32_t* perm = reinterpret_cast<const int32_t*>(sv + SL.perm);
+  const int32_t* inv = reinterpret_cast<const int32_t*>(sv + SL.inv);
+  const float* w = reinterpret_cast<const float*>(sv + SL.w);
+  const float* gu = reinterpret_cast<const float*>(sv + SL.gu);
+  const PreparedBwd P = prepared_bwd_views(prepared_bwd, E_loc, h, m, mx);
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  int32_t* koff = reinterpret_cast<int32_t*>(b + L.koff);
+  uint16_t* dA = reinterpret_cast<uint16_t*>(b + L.dA);
+  float* dgu_f32 = reinterpret_cast<float*>(b + L.dgu_f32);  // dG | dU for the transposes
+
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[i], hs);
+  };
+  mark(0);
+  e = launch_kpad_table(offsets, E_loc, wgrad_k_align(mx), koff, hs);
+  if (e == hipSuccess) e = launch_gemm_tiles(offsets, b + L.tiles, R, E_loc, hs);
+  mark(1);
+  if (e == hipSuccess)
+    e = launch_uncombine(dy, perm, w, offsets, E_loc, b + L.dO, mx ? b + L.dO_s : nullptr, R, h,
+                         k, mx, hs);
+  mark(2);
+  if (e == hipSuccess)
+    e = launch_bwd_dgrad(b + L.dO, mx ? b + L.dO_s : nullptr, offsets, P.w2b, P.w2b_s, P.w1b,
+                         P.w1b_s, gu, b + L.dgu, mx ? b + L.dgu_s : nullptr,
+                         dgu_f32, dA,
+                         b + L.tiles, R, h, m, E_loc, mx, hs, ev ? ev[3] : nullptr);
+  mark(4);
+  if (e == hipSuccess) e = launch_combine(dA, inv, nullptr, nullptr, dx, T, h, k, hs);
+  mark(5);
+  const int km = L.kmax;
+  if (e == hipSuccess)
+    e = launch_bwd_transpose(kTrX, x, perm, w, offsets, koff, E_loc, h, k, km, b + L.At,
+                             mx ? b + L.At_s : nullptr, mx, hs);
+  if (e == hipSuccess)
+    e = launch_bwd_transpose(kTrDO, dy, perm, w, offsets, koff, E_loc, h, k, km, b + L.dOt,
+                             mx ? b + L.dOt_s : nullptr, mx, hs);
+  if (e == hipSuccess)
+    e = launch_bwd_transpose(kTrH, gu, perm, w, offsets, koff, E_loc, m, k, km, b + L.Ht,
+                             mx ? b + L.Ht_s : nullptr, mx, hs);
+  if (e == hipSuccess)
+    e = launch_bwd_transpose(kTrRows, dgu_f32, perm, w, offsets, koff, E_loc, 2 * m, k, km,
+                             b + L.dGUt, mx ? b + L.dGUt_s : nullptr, mx, hs);
+  mark(6);
+  if (e == hipSuccess)
+    e = launch_bwd_wgrad(b + L.At, mx ? b + L.At_s : nullptr, b + L.dGUt,
+                         mx ? b + L.dGUt_s : nullptr, b + L.Ht, mx ? b + L.Ht_s : nullptr,
+                         b + L.dOt, mx ? b + L.dOt_s : nullptr, koff, dw_gate, dw_up, dw_down,
+                         dw_fp32 == 1, h, m, E_loc, mx, hs, ev ? ev[7] : nullptr);
+  mark(8);
   return hip_status(e);
 }
 
@@ -306,21 +477,65 @@ extern "C" {
 moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                        const uint16_t* w_router, const float* bias, const int32_t* assign,
                        const float* assign_w, const void* prepared, const void* shared_prepared,
-                       uint16_t* y, void* ws, void* stream) {
-  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y, ws,
-                      nullptr, stream);
+                       uint16_t* y, void* saved, void* ws, void* stream) {
+  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y,
+                      saved, ws, nullptr, stream);
 }
 
 moe_status moe_forward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                                 const uint16_t* w_router, const float* bias,
                                 const int32_t* assign, const float* assign_w,
                                 const void* prepared, const void* shared_prepared, uint16_t* y,
-                                void* ws, void* const* events, void* stream) {
+                                void* saved, void* ws, void* const* events, void* stream) {
   if (!events) return MOE_EINVAL;
   for (int i = 0; i < MOE_PROFILE_EVENTS; ++i)
     if (!events[i]) return MOE_EINVAL;
-  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y, ws,
-                      reinterpret_cast<const hipEvent_t*>(events), stream);
+  return forward_impl(s, dt, x, w_router, bias, assign, assign_w, prepared, shared_prepared, y,
+                      saved, ws, reinterpret_cast<const hipEvent_t*>(events), stream);
+}
+
+size_t moe_saved_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_backward_shape(s, dt) != MOE_OK) return 0;
+  return saved_layout(s).total;
+}
+
+size_t moe_prepared_bwd_weight_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_backward_shape(s, dt) != MOE_OK) return 0;
+  return prepared_bwd_bytes(s->E_loc, s->h, s->m, dt == MOE_MXFP8);
+}
+
+moe_status moe_prepare_bwd_weights(const moe_shape* s, moe_dtype dt, const uint16_t* w_gate,
+                                   const uint16_t* w_up, const uint16_t* w_down,
+                                   void* prepared_bwd, void* stream) {
+  const moe_status st = check_backward_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(w_gate) || !ok_ptr(w_up) || !ok_ptr(w_down) || !ok_ptr(prepared_bwd))
+    return MOE_EINVAL;
+  return hip_status(launch_prepare_bwd_weights(w_gate, w_up, w_down, prepared_bwd, s->E_loc, s->h,
+                                               s->m, dt == MOE_MXFP8, as_stream(stream)));
+}
+
+size_t moe_backward_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_backward_shape(s, dt) != MOE_OK) return 0;
+  return backward_layout(s, dt).total;
+}
+
+moe_status moe_backward(const moe_shape* s, moe_dtype dt, const uint16_t* x, const uint16_t* dy,
+                        const void* saved, const void* prepared_bwd, uint16_t* dx, void* dw_gate,
+                        void* dw_up, void* dw_down, int dw_fp32, void* ws, void* stream) {
+  return backward_impl(s, dt, x, dy, saved, prepared_bwd, dx, dw_gate, dw_up, dw_down, dw_fp32, ws,
+                       nullptr, stream);
+}
+
+moe_status moe_backward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                 const uint16_t* dy, const void* saved, const void* prepared_bwd,
+                                 uint16_t* dx, void* dw_gate, void* dw_up, void* dw_down,
+                                 int dw_fp32, void* ws, void* const* events, void* stream) {
+  if (!events) return MOE_EINVAL;
+  for (int i = 0; i < MOE_BWD_PROFILE_EVENTS; ++i)
+    if (!events[i]) return MOE_EINVAL;
+  return backward_impl(s, dt, x, dy, saved, prepared_bwd, dx, dw_gate, dw_up, dw_down, dw_fp32, ws,
+                       reinterpret_cast<const hipEvent_t*>(events), stream);
 }
 
 }  // extern "C"

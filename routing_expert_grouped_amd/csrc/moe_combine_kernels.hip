@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float wt[16];
   for (int j = 0; j < k; ++j) {
     src[j] = inv[(size_t)t * k + j];
-    wt[j] = w[(size_t)t * k + j];
+    wt[j] = w ? w[(size_t)t * k + j] : 1.0f;  // fma(1, o, acc) is the plain sum
   }
   const int nv = h / 8;
   for (int v = threadIdx.x; v < nv; v += 256) {

@@ -57,6 +57,34 @@ struct GemmArgs {
   int N;                        // output columns of this GEMM (weight rows per expert)
   void* out;                    // GEMM-1: H [R][N/2] (bf16 or E4M3); GEMM-2: O [R][N] bf16
   uint8_t* out_scales;          // GEMM-1 MX: H scales [R][N/64]
+  // large-tile kernel only, by epilogue mode (see EpiMode)
+  float* gu_out;                // kEpiSwiglu: G and U, float32 [R][N] in weight-row order, or null
+  const float* gu_in;           // kEpiDSwiglu: the forward's G and U, float32 [R][2N]
+  float* d_f32;                 // kEpiDSwiglu: dG and dU also as float32 [R][2N], or null
+  const int32_t* koff;          // kEpiWgrad: [E_loc+1] first K element of each expert's segment
+  int M;                        // kEpiWgrad: rows of the M-side operand per expert
+  int tiles_total;              // kEpiWgrad: E_loc * M / BM
+  int split_gate_up;            // kEpiWgrad: N is the gate/up-interleaved index (out, out2)
+  int out_f32;                  // kEpiWgrad: float32 outputs (else bf16)
+  void* out2;                   // kEpiWgrad with split_gate_up: the up half
+};
+
+// Epilogue (and grouping) modes of the large-tile kernel.
+//   kEpiSwiglu : GEMM-1 of the forward, H = silu(G) * U
+//   kEpiSwigluSave: the same, and G, U stored in float32 (gu_out) for a backward pass
+//   kEpiStore  : the accumulators as bf16 (GEMM-2 of the forward, dA of the backward)
+//   kEpiDSwiglu: dH of the backward -> dG = dH * U * silu'(G), dU = dH * silu(G) from the saved
+//                G, U; stored gate/up-interleaved per 32 (bf16, or MX per 32), plus optionally
+//                in float32 (the values the weight gradients quantise along rows)
+//   kEpiWgrad  : weight gradients. Each expert is an M x N output reduced over its own padded
+//                segment of K (its routed rows); both operands are [rows][K] per expert at the
+//                segment's offset. Tiles are (expert, M tile), N tiles as usual.
+enum EpiMode : int {
+  kEpiSwiglu = 0,
+  kEpiStore = 1,
+  kEpiDSwiglu = 2,
+  kEpiWgrad = 3,
+  kEpiSwigluSave = 4
 };
 
 __device__ __forceinline__ int swz(int row, int slot) { return slot ^ (row & 7); }
@@ -414,7 +442,7 @@ __device__ __forceinline__ void lds_barrier() {
 #define MOE_BIG_NS_MX 3
 #endif
 
-template <bool MX, bool SWIGLU, int BM, int RB, int NS>
+template <int MODE, bool MX, int BM, int RB, int NS>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   constexpr int BN = kBigBN;
   constexpr int ROWS = BN + BM;
@@ -434,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
 
   // ---- which tile: band b of band_m M tiles, XCD x takes the x-th eighth of it (N-major)
-  const int mt_total = *p.tile_count;
+  const int mt_total = MODE == kEpiWgrad ? p.tiles_total : *p.tile_count;
   const int Nt = p.N / BN;
   const int band_m = band_rows_for(Nt);
   const int x = blockIdx.x & 7;
@@ -458,10 +486,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   }
   const int pos = (x * tb >> 3) + jx;
   const int nt = pos / band_rows;
-  const int2 te = p.tiles[band * band_m + pos % band_rows];
-  const int e = te.x;
-  const int row0 = te.y;
-  const int row_end = p.offsets[e + 1];
+  const int ti = band * band_m + pos % band_rows;
+  int e, row0, row_end;
+  if constexpr (MODE == kEpiWgrad) {
+    const int mtiles = p.M / BM;
+    e = ti / mtiles;
+    row0 = (ti % mtiles) * BM;
+    row_end = p.M;
+  } else {
+    const int2 te = p.tiles[ti];
+    e = te.x;
+    row0 = te.y;
+    row_end = p.offsets[e + 1];
+  }
   const int n0 = nt * BN;
 
   const int tid = threadIdx.x;
@@ -472,8 +509,28 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   const int li = lane & 31;
   const int g = lane >> 5;
 
-  const size_t ldk = (size_t)p.K * (MX ? 1 : 2);
-  const uint8_t* wexp = p.w + (size_t)e * p.w_stride;
+  // operand bases and K of this tile: per expert for the weight operand, or the expert's segment
+  // of both operands (weight gradients)
+  constexpr size_t EL = MX ? 1 : 2;
+  int Kt = p.K;
+  const uint8_t* wexp;
+  const uint8_t* rows_b = p.rows;
+  const uint8_t* wsb = nullptr;
+  const uint8_t* rsb = p.row_scales;
+  if constexpr (MODE == kEpiWgrad) {
+    const int k0 = p.koff[e];
+    Kt = p.koff[e + 1] - k0;
+    wexp = p.w + (size_t)k0 * p.N * EL;
+    rows_b = p.rows + (size_t)k0 * p.M * EL;
+    if constexpr (MX) {
+      wsb = p.w_scales + (size_t)(k0 / kMxBlock) * p.N;
+      rsb = p.row_scales + (size_t)(k0 / kMxBlock) * p.M;
+    }
+  } else {
+    wexp = p.w + (size_t)e * p.w_stride;
+    if constexpr (MX) wsb = p.w_scales + (size_t)e * p.ws_stride;
+  }
+  const size_t ldk = (size_t)Kt * EL;
 
   // ---- DMA sources: unit id = q * 256 + tid lands at stage byte id * 16 = LDS row id / SLOTS,
   //      physical slot id % SLOTS, and must carry logical chunk slot ^ f(row). Units q < QW are
@@ -502,7 +559,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     const uint32_t off = (uint32_t)stage_off(j);
     uint8_t* b = lds + (j % NS) * STAGE + wave * 1024;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) dma16((q < QW ? wexp : p.rows) + (src[q] + off), b + q * 4096);
+    for (int q = 0; q < LOADS; ++q) dma16((q < QW ? wexp : rows_b) + (src[q] + off), b + q * 4096);
   };
 
   // ---- MX scale words. In K order, MFMA step s of a 256-element chunk multiplies blocks 2s (its
@@ -512,10 +569,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   //      step s. 32-bit offsets from the expert's and the rows' scale bases.
   uint32_t sw_off[NI], sr_off[NJ];
   int scw[NI], scr[NJ], nscw[NI], nscr[NJ];
-  const uint8_t* wsb = MX ? p.w_scales + (size_t)e * p.ws_stride : nullptr;
   const uint32_t perm_sel = g ? 0x07050301u : 0x06040200u;  // bytes g, 2+g of lo, g, 2+g of hi
   if constexpr (MX) {
-    const uint32_t nsb = (uint32_t)(p.K / kMxBlock);
+    const uint32_t nsb = (uint32_t)(Kt / kMxBlock);
 #pragma unroll
     for (int i = 0; i < NI; ++i) sw_off[i] = (uint32_t)(n0 + 128 * wn + 32 * i + li) * nsb;
 #pragma unroll
@@ -533,7 +589,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) w[i] = scale_word(wsb, sw_off[i], cc);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) r[j] = scale_word(p.row_scales, sr_off[j], cc);
+    for (int j = 0; j < NJ; ++j) r[j] = scale_word(rsb, sr_off[j], cc);
   };
 
   // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact):
@@ -621,8 +677,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     for (int k = 0; k < NM; ++k) mfma_k(F, k, sel);
   };
 
-  // ---- prologue
+  // ---- prologue (an expert segment with no rows, weight gradients only, skips the K loop and
+  //      stores zeros; the condition is uniform over the workgroup)
   Frags FA, FB;
+  if (MODE != kEpiWgrad || nk > 0) {
   if constexpr (MX) sload(0, scw, scr);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
@@ -671,12 +729,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
         const int op = (m - 1) * K + o;
         if (m >= 1 && op < NOPS) {
           if (op < NDMA) {
-            dma16((op < QW ? wexp : p.rows) + (src[op] + doff), db + op * 4096);
+            dma16((op < QW ? wexp : rows_b) + (src[op] + doff), db + op * 4096);
           } else if (op < NDMA + NSCL) {
             const int k = op - NDMA;
             if constexpr (MX) {
               if (k < NI) nscw[k] = scale_word(wsb, sw_off[k], cc_next);
-              else nscr[k - NI] = scale_word(p.row_scales, sr_off[k - NI], cc_next);
+              else nscr[k - NI] = scale_word(rsb, sr_off[k - NI], cc_next);
             }
           } else {
             load_piece(nxt, rb, rt, op - NDMA - NSCL);
@@ -753,10 +811,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   const int jsteady = max(0, (nk - NS) / PC * PC);
   run(0, jsteady, std::true_type{});
   run(jsteady, nk, std::false_type{});
+  }  // nk > 0
 
   // ---- epilogue. acc[i][j][q]: weight row n0 + 128 wn + 32 i + 8 (q / 4) + 4 g + q % 4,
   //      routed row row0 + (BM/2) wm + 32 j + li
-  if constexpr (SWIGLU) {
+  if constexpr (MODE == kEpiSwiglu || MODE == kEpiSwigluSave) {
+    if constexpr (MODE == kEpiSwigluSave) {  // G, U for a backward pass, weight-row order
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = row0 + (BM / 2) * wm + 32 * j + li;
+        if (r >= row_end) continue;
+        float* out = p.gu_out + (size_t)r * p.N + n0 + 128 * wn;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4)
+            *reinterpret_cast<f32x4_t*>(out + 32 * i + b4 * 8 + g * 4) =
+                (f32x4_t){acc[i][j][4 * b4], acc[i][j][4 * b4 + 1], acc[i][j][4 * b4 + 2],
+                          acc[i][j][4 * b4 + 3]};
+      }
+    }
     const int Hn = p.N >> 1;
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -801,7 +875,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
         }
       }
     }
-  } else {
+  } else if constexpr (MODE == kEpiStore) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int r = row0 + (BM / 2) * wm + 32 * j + li;
@@ -816,6 +890,120 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
           v.y = pack_bf16x2(acc[i][j][4 * b4 + 2], acc[i][j][4 * b4 + 3]);
           *reinterpret_cast<uint2*>(out + 32 * i + b4 * 8 + g * 4) = v;
         }
+    }
+  } else if constexpr (MODE == kEpiDSwiglu) {
+    // N = m dH columns. The 32-column tile i starting at column nb is one block of dG and one of
+    // dU; they live at interleaved columns 2 nb + [0, 32) and 2 nb + 32 + [0, 32) of the [R][2m]
+    // outputs, the same places the forward's G and U have in gu_in.
+    const int N2 = 2 * p.N;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int cg = 2 * (n0 + 128 * wn + 32 * i);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = row0 + (BM / 2) * wm + 32 * j + li;
+        const int rr = r < row_end ? r : row_end - 1;  // rows past the expert's end: loads only
+        const float* gu = p.gu_in + (size_t)rr * N2 + cg + 4 * g;
+        float dg[16], du[16];
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const f32x4_t G = *reinterpret_cast<const f32x4_t*>(gu + 8 * b4);
+          const f32x4_t U = *reinterpret_cast<const f32x4_t*>(gu + 32 + 8 * b4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dh = acc[i][j][4 * b4 + q];
+            const float sg = 1.0f / (1.0f + expf(-G[q]));
+            const float silu = G[q] * sg;
+            const float dsilu = sg * (1.0f + G[q] * (1.0f - sg));
+            dg[4 * b4 + q] = dh * U[q] * dsilu;
+            du[4 * b4 + q] = dh * silu;
+          }
+        }
+        if constexpr (MX) {
+          float ag = 0.0f, au = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            ag = fmaxf(ag, fabsf(dg[q]));
+            au = fmaxf(au, fabsf(du[q]));
+          }
+          ag = fmaxf(ag, __shfl_xor(ag, 32));  // the other 16 columns of each block
+          au = fmaxf(au, __shfl_xor(au, 32));
+          const int sg_ = mx_block_exponent(ag), su_ = mx_block_exponent(au);
+          const float ig = mx_inv_scale(sg_), iu = mx_inv_scale(su_);
+          if (r < row_end) {
+            uint8_t* out = reinterpret_cast<uint8_t*>(p.out) + (size_t)r * N2 + cg + 4 * g;
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+              const float* a4 = dg + 4 * b4;
+              const float* c4 = du + 4 * b4;
+              *reinterpret_cast<uint32_t*>(out + 8 * b4) =
+                  e4m3_encode(a4[0] * ig) | (e4m3_encode(a4[1] * ig) << 8) |
+                  (e4m3_encode(a4[2] * ig) << 16) | (e4m3_encode(a4[3] * ig) << 24);
+              *reinterpret_cast<uint32_t*>(out + 32 + 8 * b4) =
+                  e4m3_encode(c4[0] * iu) | (e4m3_encode(c4[1] * iu) << 8) |
+                  (e4m3_encode(c4[2] * iu) << 16) | (e4m3_encode(c4[3] * iu) << 24);
+            }
+            // scale bytes of the dG block (lane group 0) and the dU block (lane group 1)
+            p.out_scales[(size_t)r * (N2 / kMxBlock) + (cg >> 5) + g] = (uint8_t)((g ? su_ : sg_) + 127);
+          }
+        } else {
+          if (r < row_end) {
+            uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (size_t)r * N2 + cg + 4 * g;
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+              *reinterpret_cast<uint2*>(ob + 8 * b4) =
+                  make_uint2(pack_bf16x2(dg[4 * b4], dg[4 * b4 + 1]),
+                             pack_bf16x2(dg[4 * b4 + 2], dg[4 * b4 + 3]));
+              *reinterpret_cast<uint2*>(ob + 32 + 8 * b4) =
+                  make_uint2(pack_bf16x2(du[4 * b4], du[4 * b4 + 1]),
+                             pack_bf16x2(du[4 * b4 + 2], du[4 * b4 + 3]));
+            }
+          }
+        }
+        if (p.d_f32 && r < row_end) {
+          float* of = p.d_f32 + (size_t)r * N2 + cg + 4 * g;
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            *reinterpret_cast<f32x4_t*>(of + 8 * b4) =
+                (f32x4_t){dg[4 * b4], dg[4 * b4 + 1], dg[4 * b4 + 2], dg[4 * b4 + 3]};
+            *reinterpret_cast<f32x4_t*>(of + 32 + 8 * b4) =
+                (f32x4_t){du[4 * b4], du[4 * b4 + 1], du[4 * b4 + 2], du[4 * b4 + 3]};
+          }
+        }
+      }
+    }
+  } else {  // kEpiWgrad: out[e][r][n] of an M x N matrix per expert (or split gate / up halves)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int nb = n0 + 128 * wn + 32 * i;
+      void* o = p.out;
+      int col = nb, ld = p.N;
+      if (p.split_gate_up) {  // N index: blocks of 32 alternate gate and up columns
+        o = ((nb >> 5) & 1) ? p.out2 : p.out;
+        col = (nb >> 6) * 32;
+        ld = p.N >> 1;
+      }
+      const size_t ebase = (size_t)e * p.M * ld;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = row0 + (BM / 2) * wm + 32 * j + li;
+        const size_t at = ebase + (size_t)r * ld + col + 4 * g;
+        if (p.out_f32) {
+          float* of = reinterpret_cast<float*>(o) + at;
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4)
+            *reinterpret_cast<f32x4_t*>(of + 8 * b4) =
+                (f32x4_t){acc[i][j][4 * b4], acc[i][j][4 * b4 + 1], acc[i][j][4 * b4 + 2],
+                          acc[i][j][4 * b4 + 3]};
+        } else {
+          uint16_t* ob = reinterpret_cast<uint16_t*>(o) + at;
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4)
+            *reinterpret_cast<uint2*>(ob + 8 * b4) =
+                make_uint2(pack_bf16x2(acc[i][j][4 * b4], acc[i][j][4 * b4 + 1]),
+                           pack_bf16x2(acc[i][j][4 * b4 + 2], acc[i][j][4 * b4 + 3]));
+        }
+      }
     }
   }
 }
@@ -952,8 +1140,8 @@ bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 
 FfnLayout ffn_layout(int R, int h, int m, int E_loc, bool mx) {
   FfnLayout L{};
-  const int bm = ffn_tile_rows(R, h, m, E_loc, mx);
-  L.max_tiles = (R + bm - 1) / bm + E_loc;
+  // room for 128-row tiles, the smallest any launch takes
+  L.max_tiles = (R + kBM - 1) / kBM + E_loc;
   size_t off = 0;
   L.count = off;
   off = align_up(off + sizeof(int));
@@ -1010,19 +1198,40 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
   return hipGetLastError();
 }
 
+// kernels launched by name in non-template functions, so that each instantiation is compiled for
+// the device
+#define MOE_BIG(MODEV, MXV, BMV, G, A)                                                          \
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV,                                  \
+                                              (MXV ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16),          \
+                                              (MXV ? MOE_BIG_NS_MX                              \
+                                                   : (BMV == 128 ? MOE_BIG_NS_BF16_128          \
+                                                                 : MOE_BIG_NS_BF16))>),         \
+                     G, dim3(256), 0, st, A)
+
+// grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most
+// ceil(tiles / 8) plus one per band, and a multiple of 8 for the XCD remap
+static dim3 big_grid(int max_mt, int nt) {
+  return dim3(8 * ((max_mt * nt + 7) / 8 + max_mt / band_rows_for(nt) + 2));
+}
+
 hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
                              const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
-                             int m, int E_loc, bool mx, hipStream_t st, const hipEvent_t* ev) {
+                             int m, int E_loc, bool mx, hipStream_t st, const hipEvent_t* ev,
+                             float* gu_out) {
+  const bool save = gu_out != nullptr;
+  // a forward that keeps G and U takes 128-row tiles (the 256-row BF16 variant with the extra
+  // stores does not fit the register file)
+  const int bm = save ? kBM : ffn_tile_rows(R, h, m, E_loc, mx);
+  const int max_tiles = (R + bm - 1) / bm + E_loc;
   const PreparedLayout P = prepared_layout(E_loc, h, m, mx);
   const FfnLayout F = ffn_layout(R, h, m, E_loc, mx);
-  const int bm = ffn_tile_rows(R, h, m, E_loc, mx);
   const bool big = ffn_big(h, m);
   const uint8_t* pw = reinterpret_cast<const uint8_t*>(prepared);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   int2* tiles = reinterpret_cast<int2*>(w + F.tiles);
   int* tile_count = reinterpret_cast<int*>(w + F.count);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, E_loc, bm,
-                     F.max_tiles, tiles, tile_count);
+                     max_tiles, tiles, tile_count);
   if (ev) (void)hipEventRecord(ev[0], st);
   const size_t el = mx ? 1 : 2;
 
@@ -1040,6 +1249,7 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   a1.N = 2 * m;
   a1.out = w + F.H;
   a1.out_scales = mx ? w + F.Hs : nullptr;
+  a1.gu_out = gu_out;
 
   GemmArgs a2{};
   a2.rows = w + F.H;
@@ -1057,38 +1267,29 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   a2.out_scales = nullptr;
 
   if (big) {
-    // the XCD remap needs the grid rounded up to a multiple of 8
-    // per XCD at most ceil(tiles / 8) plus one per band: the grid covers 8 times that
-    auto big_grid = [&](int nt) {
-      return dim3(8 * ((F.max_tiles * nt + 7) / 8 + F.max_tiles / band_rows_for(nt) + 2));
-    };
-    const dim3 g1 = big_grid((2 * m) / kBigBN), g2 = big_grid(h / kBigBN);
-    // kernels launched by name here so that each instantiation is compiled for the device
-#define MOE_BIG(MXV, SW, BMV, G, A)                                                             \
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<MXV, SW, BMV, (MXV ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16), \
-                                                (MXV ? MOE_BIG_NS_MX                            \
-                                                     : (BMV == 128 ? MOE_BIG_NS_BF16_128        \
-                                                                   : MOE_BIG_NS_BF16))>),       \
-                       G, dim3(256), 0, st, A)
+    const dim3 g1 = big_grid(max_tiles, (2 * m) / kBigBN);
+    const dim3 g2 = big_grid(max_tiles, h / kBigBN);
     if (mx) {  // MXFP8 always takes 128-row tiles
-      MOE_BIG(true, true, 128, g1, a1);
+      if (save) MOE_BIG(kEpiSwigluSave, true, 128, g1, a1);
+      else MOE_BIG(kEpiSwiglu, true, 128, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
-      MOE_BIG(true, false, 128, g2, a2);
-    } else if (bm == 256) {
-      MOE_BIG(false, true, 256, g1, a1);
+      MOE_BIG(kEpiStore, true, 128, g2, a2);
+    } else if (bm == 256) {  // never with save
+      MOE_BIG(kEpiSwiglu, false, 256, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
-      MOE_BIG(false, false, 256, g2, a2);
+      MOE_BIG(kEpiStore, false, 256, g2, a2);
     } else {
-      MOE_BIG(false, true, 128, g1, a1);
+      if (save) MOE_BIG(kEpiSwigluSave, false, 128, g1, a1);
+      else MOE_BIG(kEpiSwiglu, false, 128, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
-      MOE_BIG(false, false, 128, g2, a2);
+      MOE_BIG(kEpiStore, false, 128, g2, a2);
     }
-#undef MOE_BIG
     if (ev) (void)hipEventRecord(ev[2], st);
     return hipGetLastError();
   }
-  dim3 grid1(F.max_tiles, (2 * m) / kBN);
-  dim3 grid2(F.max_tiles, h / kBN);
+  if (gu_out) return hipErrorInvalidValue;  // G and U are only kept by the large-tile kernel
+  dim3 grid1(max_tiles, (2 * m) / kBN);
+  dim3 grid2(max_tiles, h / kBN);
   if (mx)
     hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), grid1, dim3(kThreads), 0, st, a1);
   else
@@ -1101,5 +1302,123 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   if (ev) (void)hipEventRecord(ev[2], st);
   return hipGetLastError();
 }
+
+// the backward's routed-row GEMMs take 128-row tiles in both precisions (their epilogues do not
+// fit the register file next to 256-row accumulators)
+constexpr int kBwdBM = 128;
+
+size_t gemm_tiles_bytes(int R, int E_loc) {
+  return align_up(sizeof(int)) + (size_t)((R + kBwdBM - 1) / kBwdBM + E_loc) * sizeof(int2);
+}
+
+hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc,
+                             hipStream_t st) {
+  const int bm = kBwdBM;
+  const int max_tiles = (R + bm - 1) / bm + E_loc;
+  uint8_t* tw = reinterpret_cast<uint8_t*>(tiles_ws);
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, E_loc, bm, max_tiles,
+                     reinterpret_cast<int2*>(tw + align_up(sizeof(int))),
+                     reinterpret_cast<int*>(tw));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* offsets,
+                            const uint8_t* w2b, const uint8_t* w2b_s, const uint8_t* w1b,
+                            const uint8_t* w1b_s, const float* gu, void* dgu, uint8_t* dgu_s,
+                            float* dgu_f32, uint16_t* dA, const void* tiles_ws, int R, int h,
+                            int m, int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid) {
+  if (!ffn_big(h, m) || m % kBigBN) return hipErrorInvalidValue;
+  const int max_tiles = (R + kBwdBM - 1) / kBwdBM + E_loc;
+  const uint8_t* tw = reinterpret_cast<const uint8_t*>(tiles_ws);
+  const int* tile_count = reinterpret_cast<const int*>(tw);
+  const int2* tiles = reinterpret_cast<const int2*>(tw + align_up(sizeof(int)));
+  const size_t el = mx ? 1 : 2;
+
+  // dH = dO W_down^T (K = h, N = m) with the SwiGLU backward in the epilogue -> dG | dU
+  GemmArgs a{};
+  a.rows = reinterpret_cast<const uint8_t*>(dO);
+  a.row_scales = dO_s;
+  a.w = w2b;
+  a.w_scales = w2b_s;
+  a.w_stride = (size_t)m * h * el;
+  a.ws_stride = (size_t)m * (h / kMxBlock);
+  a.offsets = offsets;
+  a.tiles = tiles;
+  a.tile_count = tile_count;
+  a.K = h;
+  a.N = m;
+  a.out = dgu;
+  a.out_scales = dgu_s;
+  a.gu_in = gu;
+  a.d_f32 = dgu_f32;
+
+  // dA = [dG | dU] [W_gate | W_up]^T (K = 2m, interleaved per 32 on both sides, N = h)
+  GemmArgs b{};
+  b.rows = reinterpret_cast<const uint8_t*>(dgu);
+  b.row_scales = dgu_s;
+  b.w = w1b;
+  b.w_scales = w1b_s;
+  b.w_stride = (size_t)h * 2 * m * el;
+  b.ws_stride = (size_t)h * (2 * m / kMxBlock);
+  b.offsets = offsets;
+  b.tiles = tiles;
+  b.tile_count = tile_count;
+  b.K = 2 * m;
+  b.N = h;
+  b.out = dA;
+
+  const dim3 ga = big_grid(max_tiles, m / kBigBN), gb = big_grid(max_tiles, h / kBigBN);
+  if (mx) MOE_BIG(kEpiDSwiglu, true, kBwdBM, ga, a);
+  else MOE_BIG(kEpiDSwiglu, false, kBwdBM, ga, a);
+  if (ev_mid) (void)hipEventRecord(ev_mid, st);
+  if (mx) MOE_BIG(kEpiStore, true, kBwdBM, gb, b);
+  else MOE_BIG(kEpiStore, false, kBwdBM, gb, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_t* dGUt,
+                            const uint8_t* dGUt_s, const uint8_t* Ht, const uint8_t* Ht_s,
+                            const uint8_t* dOt, const uint8_t* dOt_s, const int32_t* koff,
+                            void* dw_gate, void* dw_up, void* dw_down, bool out_f32, int h, int m,
+                            int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid) {
+  if (h % kBigBN || m % kBigBN) return hipErrorInvalidValue;
+  const int bm = mx ? 128 : 256;
+  // dW_gate | dW_up [e] (h x 2m) = A_e^T [dG | dU]_e: M side A^T (h rows), N side [dG | dU]^T
+  GemmArgs a{};
+  a.rows = At;
+  a.row_scales = At_s;
+  a.w = dGUt;
+  a.w_scales = dGUt_s;
+  a.koff = koff;
+  a.M = h;
+  a.N = 2 * m;
+  a.tiles_total = E_loc * (h / bm);
+  a.split_gate_up = 1;
+  a.out_f32 = out_f32;
+  a.out = dw_gate;
+  a.out2 = dw_up;
+  // dW_down [e] (m x h) = H_e^T dO_e: M side H^T (m rows), N side dO^T (h rows)
+  GemmArgs b{};
+  b.rows = Ht;
+  b.row_scales = Ht_s;
+  b.w = dOt;
+  b.w_scales = dOt_s;
+  b.koff = koff;
+  b.M = m;
+  b.N = h;
+  b.tiles_total = E_loc * (m / bm);
+  b.split_gate_up = 0;
+  b.out_f32 = out_f32;
+  b.out = dw_down;
+  const dim3 ga = big_grid(a.tiles_total, a.N / kBigBN), gb = big_grid(b.tiles_total, b.N / kBigBN);
+  if (mx) MOE_BIG(kEpiWgrad, true, 128, ga, a);
+  else MOE_BIG(kEpiWgrad, false, 256, ga, a);
+  if (ev_mid) (void)hipEventRecord(ev_mid, st);
+  if (mx) MOE_BIG(kEpiWgrad, true, 128, gb, b);
+  else MOE_BIG(kEpiWgrad, false, 256, gb, b);
+  return hipGetLastError();
+}
+
+#undef MOE_BIG
 
 }  // namespace moe

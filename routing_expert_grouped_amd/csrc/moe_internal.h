@@ -114,13 +114,66 @@ size_t prepared_bytes(int E_loc, int h, int m, bool mx);
 hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
                                   const uint16_t* w_down, void* prepared, int E_loc, int h, int m,
                                   bool mx, hipStream_t st);
-// ev (optional): three events recorded after the tile table, GEMM-1 and GEMM-2
+// ev (optional): three events recorded after the tile table, GEMM-1 and GEMM-2.
+// gu_out (optional, large-tile shapes only): GEMM-1's G and U as float32 [R][2m], gate/up
+// interleaved per 32 like the prepared W1 rows, kept for a backward pass.
 hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
                              const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
                              int m, int E_loc, bool mx, hipStream_t st,
-                             const hipEvent_t* ev = nullptr);
+                             const hipEvent_t* ev = nullptr, float* gu_out = nullptr);
 
-// Combine (moe_combine_kernels.hip)
+// Backward GEMMs (moe_gemm_kernels.hip). Both need h % 256 == 0 and m % 256 == 0.
+// K segments of the weight gradients: each expert's routed rows padded to a multiple of this
+inline int wgrad_k_align(bool mx) { return mx ? 256 : 64; }
+// the M-tile table of the backward's routed-row GEMMs (count + tiles) and its size
+size_t gemm_tiles_bytes(int R, int E_loc);
+hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc,
+                             hipStream_t st);
+// dG|dU (with the SwiGLU backward) from dO and the prepared W_down rows [e][m][h], then dA from
+// dG|dU and the prepared [W_gate | W_up] rows [e][h][2m]; ev_mid (or null) between the two.
+// gu: the forward's G | U (float32); dgu: bf16 or E4M3 (+ dgu_s); dgu_f32: the same in float32
+hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* offsets,
+                            const uint8_t* w2b, const uint8_t* w2b_s, const uint8_t* w1b,
+                            const uint8_t* w1b_s, const float* gu, void* dgu, uint8_t* dgu_s,
+                            float* dgu_f32, uint16_t* dA, const void* tiles_ws, int R, int h,
+                            int m, int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid);
+// weight gradients from the per-expert transposed operands ([C][kpad_e] at koff[e] * C)
+hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_t* dGUt,
+                            const uint8_t* dGUt_s, const uint8_t* Ht, const uint8_t* Ht_s,
+                            const uint8_t* dOt, const uint8_t* dOt_s, const int32_t* koff,
+                            void* dw_gate, void* dw_up, void* dw_down, bool out_f32, int h, int m,
+                            int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid);
+
+// Backward data movement (moe_backward_kernels.hip)
+size_t prepared_bwd_bytes(int E_loc, int h, int m, bool mx);
+struct PreparedBwd {
+  const uint8_t *w1b, *w1b_s, *w2b, *w2b_s;
+};
+PreparedBwd prepared_bwd_views(const void* prepared_bwd, int E_loc, int h, int m, bool mx);
+hipError_t launch_prepare_bwd_weights(const uint16_t* w_gate, const uint16_t* w_up,
+                                      const uint16_t* w_down, void* prepared_bwd, int E_loc,
+                                      int h, int m, bool mx, hipStream_t st);
+// koff[0..E_loc]: exclusive scan of the expert row counts rounded up to `align`
+hipError_t launch_kpad_table(const int32_t* offsets, int E_loc, int align, int32_t* koff,
+                             hipStream_t st);
+// dO[r] = w[perm[r]] * dY[perm[r] / k] for the routed rows, bf16 or MX per 32 along h
+hipError_t launch_uncombine(const uint16_t* dy, const int32_t* perm, const float* w,
+                            const int32_t* offsets, int E_loc, void* dO, uint8_t* dO_s, int R,
+                            int h, int k, bool mx, hipStream_t st);
+// Sources of the per-expert transposes ([C][kpad_e] per expert, MX per 32 along the rows)
+enum TransposeSrc : int {
+  kTrX = 0,      // x[perm[r] / k], bf16                        (C = h)
+  kTrDO = 1,     // w[perm[r]] * dY[perm[r] / k], dY bf16       (C = h)
+  kTrH = 2,      // silu(G) * U from the saved float32 G | U    (C = m)
+  kTrRows = 3,   // row r of a float32 [R][C] matrix            (C = 2m: dG | dU)
+};
+// rows_max: an upper bound of koff[E_loc] (R + E_loc * (align - 1))
+hipError_t launch_bwd_transpose(int src_kind, const void* src, const int32_t* perm,
+                                const float* w, const int32_t* offsets, const int32_t* koff,
+                                int E_loc, int C, int k, int rows_max, uint8_t* dst,
+                                uint8_t* dst_s, bool mx, hipStream_t st);
+
+// Combine (moe_combine_kernels.hip); w == nullptr: every weight is 1 (the backward's un-permute)
 hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,
                           const uint16_t* shared_out, uint16_t* y, int T, int h, int k,
                           hipStream_t st);

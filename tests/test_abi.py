@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     L = lib.load()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for code in range(4):
         assert L.moe_status_string(code).decode().startswith("MOE_")
 
@@ -109,14 +109,19 @@ def test_expert_path_validation(lib):
         lib.MOE_EUNSUPPORTED
     assert L.moe_combine(ctypes.byref(ok), P, P, None, None, P, None) == lib.MOE_EINVAL
     # forward: router and share arguments are exclusive; shared expert consistency
-    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, P, P, P, None, P, P, None) == \
+    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, P, P, P, None, P, None, P, None) == \
         lib.MOE_EINVAL
-    assert L.moe_forward(ctypes.byref(ok), 0, P, None, None, None, None, P, None, P, P, None) == \
-        lib.MOE_EINVAL
+    assert L.moe_forward(ctypes.byref(ok), 0, P, None, None, None, None, P, None, P, None, P,
+                         None) == lib.MOE_EINVAL
     assert L.moe_forward(ctypes.byref(_shape(lib, m_shared=128)), 0, P, P, None, None, None, P,
-                         None, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, None, None, P, None, P, None, None) == \
-        lib.MOE_EINVAL
+                         None, P, None, P, None) == lib.MOE_EINVAL
+    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, None, None, P, None, P, None, None,
+                         None) == lib.MOE_EINVAL
+    # a training forward (saved != NULL) needs m % 256 == 0 and an aligned buffer
+    assert L.moe_forward(ctypes.byref(ok), 0, P, P, None, None, None, P, None, P, P, P, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_forward(ctypes.byref(_shape(lib, m=256)), 0, P, P, None, None, None, P, None, P,
+                         P + 8, P, None) == lib.MOE_EINVAL
     # prepare weights
     assert L.moe_prepare_weights(ctypes.byref(ok), 0, P, P, None, P, None) == lib.MOE_EINVAL
 
@@ -131,3 +136,30 @@ def test_views_are_host_arithmetic(lib):
     assert all(p % 256 == 0 and base <= p < base + L.moe_forward_workspace_bytes(
         ctypes.byref(s), 0) for p in ptrs)
     assert v.row_scales is None and v.shared_out is None and v.logits is not None
+
+
+def test_backward_sizes_and_validation(lib):
+    L = lib.load()
+    P = FAKE
+    ok = _shape(lib, m=256)
+    R, h, m, E = 128, 256, 256, 8
+    for dt in (0, 1):
+        el = 2 if dt == 0 else 1
+        assert L.moe_saved_bytes(ctypes.byref(ok), dt) >= R * (12 + 2 * m * 2)
+        assert L.moe_prepared_bwd_weight_bytes(ctypes.byref(ok), dt) >= 3 * E * h * m * el
+        assert L.moe_backward_workspace_bytes(ctypes.byref(ok), dt) > R * h * 2
+        # m % 256 != 0: not covered by the backward
+        assert L.moe_saved_bytes(ctypes.byref(_shape(lib, m=128)), dt) == 0
+        assert L.moe_backward_workspace_bytes(ctypes.byref(_shape(lib, m=128)), dt) == 0
+    args = [P, P, P, P, P, P, P, P]  # x dy saved prepared_bwd dx dw_gate dw_up dw_down
+    assert L.moe_backward(ctypes.byref(ok), 0, *args, 2, P, None) == lib.MOE_EINVAL
+    assert L.moe_backward(ctypes.byref(ok), 0, P, P, None, P, P, P, P, P, 1, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_backward(ctypes.byref(ok), 1, P, P, P, P, P, P, P, P + 4, 1, P, None) == \
+        lib.MOE_EINVAL
+    assert L.moe_backward(ctypes.byref(_shape(lib, m=128)), 0, *args, 1, P, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_backward_profiled(ctypes.byref(ok), 0, *args, 1, P, None, None) == \
+        lib.MOE_EINVAL  # no events
+    assert L.moe_prepare_bwd_weights(ctypes.byref(_shape(lib, h=384)), 0, P, P, P, P, None) == \
+        lib.MOE_EUNSUPPORTED
