@@ -8,7 +8,10 @@ none of the method's arithmetic.
 
 It is written to be read against the pages, not to be fast: plain NumPy in float64 (float32 only
 where a fixed float32 order is itself the definition, see ``router_logits_fixed_order``), one
-expert at a time, no blocking, fusion or reordering beyond what each definition states.
+expert at a time, no blocking, fusion or reordering beyond what each definition states. The one
+piece in C is the per-element E4M3 encoding and the per-block MX scale (``mx_codec.c``, plain loops
+over elements and blocks, compiled with gcc without fast-math), so that the full-size weight
+matrices can be quantised in seconds; ``formats.py`` states what it computes.
 
 Sources. The method is the Mixture-of-Kittens MoE layer described on the page "Mixture-of-Kittens:
 Cursor's Open-Source MoE Training Megakernel for NVL72" (sections TL;DR, the flowchart, Key claims)

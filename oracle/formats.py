@@ -22,6 +22,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import _native
+
 MX_BLOCK = 32
 E4M3_EMAX = 8  # exponent of the largest normal, 448 = 1.75 * 2**8
 E4M3_MAX = 448.0
@@ -39,9 +41,9 @@ def bf16_to_f32(u: np.ndarray) -> np.ndarray:
     return (u.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
     """E4M3 byte -> float64 value, straight from the bit-field definition (NaN for S.1111.111)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    c = np.asarray(c, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     ex = (c >> 3) & 0xF
     man = (c & 0x7).astype(np.float64)
@@ -51,35 +53,25 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
+_E4M3_VALUES = _e4m3_value(np.arange(256))  # the value of every byte
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 byte -> float64 value (the bit-field definition, evaluated once for all 256 bytes)."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
 def e4m3_encode(y: np.ndarray) -> np.ndarray:
     """float64 -> E4M3 byte: round to nearest even, saturate at 448, keep the sign of zero.
 
     Normal range: with |y| = f * 2**e, 1 <= f < 2, the mantissa code is round(|y| * 2**(3 - e)) - 8;
     a rounding up to 16 carries into the exponent. Below 2**-6 the grid is n * 2**-9, n = 0..8,
-    and n = 8 is the smallest normal (code 0x08).
+    and n = 8 is the smallest normal (code 0x08). The loop over elements is in mx_codec.c.
     """
-    y = np.asarray(y, dtype=np.float64)
-    neg = np.signbit(y)
-    a = np.abs(y)
-    code = np.zeros(a.shape, dtype=np.int64)
-
-    sub = a < 2.0 ** -6
-    n_sub = np.rint(np.where(sub, a, 0.0) * 2.0 ** 9)  # rint: half to even
-    code = np.where(sub, n_sub.astype(np.int64), code)  # n_sub == 8 is code 0x08, the min normal
-
-    _, ex = np.frexp(np.where(sub, 1.0, a))  # a = f * 2**ex, 0.5 <= f < 1
-    e = ex.astype(np.int64) - 1
-    n = np.rint(np.where(sub, 8.0, a) * np.exp2((3 - e).astype(np.float64))).astype(np.int64)
-    carry = n == 16
-    e = np.where(carry, e + 1, e)
-    n = np.where(carry, 8, n)
-    nor_code = ((e + 7) << 3) | (n - 8)
-    code = np.where(sub, code, nor_code)
-
-    code = np.where(a >= E4M3_MAX, 0x7E, code)
-    code = np.minimum(code, 0x7E)  # never produce the NaN pattern
-    code = code | np.where(neg, 0x80, 0)
-    return code.astype(np.uint8)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.uint8)
+    _native.lib().oracle_e4m3_encode(y.ctypes.data, out.ctypes.data, y.size)
+    return out
 
 
 def mx_quantize(v: np.ndarray, axis: int = -1):
@@ -87,20 +79,22 @@ def mx_quantize(v: np.ndarray, axis: int = -1):
 
     Returns (codes uint8, same shape as v; scales uint8, shape with that axis divided by 32).
     The length along ``axis`` must be a multiple of 32.
+
+    Per block: s = floor(log2 amax) - 8 (amax > 0), clamped to [-127, 127], else -127; every
+    element is divided by 2**s and encoded with e4m3_encode. The loop over blocks is in
+    mx_codec.c.
     """
-    v = np.asarray(v, dtype=np.float64)
-    v = np.moveaxis(v, axis, -1)
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
     n = v.shape[-1]
     if n % MX_BLOCK:
         raise ValueError("MX blocks need a length that is a multiple of 32")
-    blocks = v.reshape(v.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
-    amax = np.max(np.abs(blocks), axis=-1)
-    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))  # floor(log2 amax) = ex - 1, exactly
-    s = np.where(amax > 0, ex.astype(np.int64) - 1 - E4M3_EMAX, -E8M0_BIAS)
-    s = np.clip(s, -E8M0_BIAS, E8M0_BIAS)
-    y = blocks * np.exp2(-s.astype(np.float64))[..., None]
-    codes = e4m3_encode(y).reshape(v.shape)
-    scales = (s + E8M0_BIAS).astype(np.uint8)
+    rows = np.ascontiguousarray(v).reshape(-1, n)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    scales = np.empty((rows.shape[0], n // MX_BLOCK), dtype=np.uint8)
+    _native.lib().oracle_mx_quantize_rows(rows.ctypes.data, rows.shape[0], n, codes.ctypes.data,
+                                          scales.ctypes.data)
+    codes = codes.reshape(v.shape)
+    scales = scales.reshape(v.shape[:-1] + (n // MX_BLOCK,))
     return np.moveaxis(codes, -1, axis), np.moveaxis(scales, -1, axis)
 
 

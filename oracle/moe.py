@@ -363,3 +363,46 @@ def layer_backward(wl, inp: dict, fwd: dict, weights_of, dy_f64=None, mx=None):
         sel = invk[:, j] >= 0
         dX[sel] += dA[invk[sel, j]]
     return dX, dW
+
+
+def token_input_grads(wl, inp: dict, tokens, weights_of, dy_f64=None, mx=None) -> np.ndarray:
+    """dX[t] for a few tokens only. The input gradient of a routed row depends only on that row
+    (its dgrad GEMMs reduce along h and m, never across rows), so a token's dX needs only its own
+    k rows: for each slot j, expert_backward of the single row x[t] with dO = w[t, j] dY[t]."""
+    if mx is None:
+        mx = wl.dtype == "mxfp8"
+    tokens = np.asarray(tokens, dtype=np.int64)
+    dy = bf16_to_f64(inp["dy"]) if dy_f64 is None else dy_f64
+    x64 = bf16_to_f64(inp["x"][tokens])
+    if wl.mode == "router":
+        _, idx, w = route(inp["x"][tokens], inp["w_router"], inp["bias"], wl.k)
+    else:
+        idx = inp["assign"].reshape(-1, wl.k)[tokens]
+        w = inp["assign_w"].reshape(-1, wl.k)[tokens].astype(np.float64)
+    out = np.zeros((len(tokens), wl.h), dtype=np.float64)
+    for i, t in enumerate(tokens):
+        for j in range(wl.k):
+            e = int(idx[i, j])
+            if not 0 <= e < wl.E_loc:
+                continue
+            wg, wu, wd = (bf16_to_f64(v) for v in weights_of(e))
+            dA = expert_backward(x64[i:i + 1], w[i, j] * dy[t][None, :], wg, wu, wd, mx=mx)[0]
+            out[i] += dA[0]
+    return out
+
+
+def expert_weight_grads(wl, inp: dict, assign: np.ndarray, assign_w: np.ndarray, e: int,
+                        weights_of, dy_f64=None, mx=None):
+    """(dW_gate, dW_up, dW_down) of one expert only. They reduce over the expert's routed rows,
+    in the schedule's order (its assignments ascending), so only those rows are needed.
+    assign / assign_w: the local expert and gate weight of every assignment (length T*k)."""
+    if mx is None:
+        mx = wl.dtype == "mxfp8"
+    dy = bf16_to_f64(inp["dy"]) if dy_f64 is None else dy_f64
+    a_idx = np.nonzero(np.asarray(assign) == e)[0]  # ascending: the stable schedule's row order
+    tok = a_idx // wl.k
+    a = bf16_to_f64(inp["x"][tok])
+    dO = np.asarray(assign_w, dtype=np.float64)[a_idx][:, None] * dy[tok]
+    wg, wu, wd = (bf16_to_f64(v) for v in weights_of(e))
+    _, dwg, dwu, dwd = expert_backward(a, dO, wg, wu, wd, mx=mx)
+    return dwg, dwu, dwd

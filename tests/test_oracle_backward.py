@@ -147,3 +147,27 @@ def test_layer_backward_assembles_experts_and_unpermutes(mx):
             acc += dA[list(rows).index(t * wl.k + j)]
         assert np.allclose(dX[t], acc, rtol=1e-12, atol=1e-12)
     assert len(dW) == 4 and dW[0][0].shape == (64, 32) and dW[0][2].shape == (32, 64)
+
+
+@pytest.mark.parametrize("mode,mx", [("router", False), ("router", True), ("share", True)])
+def test_sampled_gradients_match_whole_layer(mode, mx):
+    kw = dict(name="t", T=40, h=64, m=64, E=4, k=2, E_loc=4, dtype="mxfp8" if mx else "bf16",
+              mode=mode, backward=True)
+    if mode == "share":
+        kw.update(E=384, E_loc=3, k=3, zipf_s=1.0)
+    wl = I.Workload(**kw)
+    inp = I.make_inputs(wl, seed=8)
+    cache = {e: I.expert_weights(wl, e, seed=8) for e in range(wl.E_loc)}
+    fwd = M.layer_forward(wl, inp, cache.__getitem__, keep=True)
+    dX, dW = M.layer_backward(wl, inp, fwd, cache.__getitem__)
+    toks = [0, 17, 39]
+    got = M.token_input_grads(wl, inp, toks, cache.__getitem__)
+    assert np.allclose(got, dX[toks], rtol=1e-12, atol=1e-12)
+    if mode == "router":
+        assign, aw = fwd["idx"].reshape(-1), fwd["w"].reshape(-1)
+    else:
+        assign, aw = inp["assign"], inp["assign_w"]
+    for e in range(wl.E_loc):
+        g = M.expert_weight_grads(wl, inp, assign, aw, e, cache.__getitem__)
+        for i in range(3):
+            assert np.allclose(g[i], dW[e][i], rtol=1e-12, atol=1e-12), (e, i)
