@@ -42,6 +42,8 @@ def parse():
                     help="tokens of the oracle's timed sample (0 disables the CPU baseline)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much wall time has run")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward timing of workloads that define one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
@@ -135,6 +137,56 @@ def cpu_baseline(wl, inp, weights_host, shared_host, n_tokens: int, min_seconds:
                       f"expert's SwiGLU FFN + combine), {passes} pass(es), {dt:.1f} s wall"}
 
 
+def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
+    """The expert-path backward of the same layer, timed on its own: one forward that keeps its
+    saved state (timed too, as the training forward), then K backward steps from that state, each
+    with HIP events at its stage boundaries. Weight gradients in float32."""
+    import torch
+
+    dev = x.device
+    saved = torch.empty(G.moe_saved_bytes(sh, wl.dtype), dtype=torch.uint8, device=dev)
+    pbwd = G.moe_prepare_bwd_weights(sh, wl.dtype, wg, wu, wd)
+    dy = torch.from_numpy(inp["dy"].view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(G.moe_forward_workspace_bytes(sh, wl.dtype), dtype=torch.uint8, device=dev)
+    fev = G.HipEvents()
+    for _ in range(2):
+        G.moe_forward_profiled(sh, wl.dtype, x, prepared, fev, y=y, ws=ws, saved=saved, **kw)
+    torch.cuda.synchronize()
+    fwd_saved_ms = fev.elapsed_ms(0, G.MOE_PROFILE_EVENTS - 1)
+    fev.close()
+    dx = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device=dev)
+    dw = (torch.empty(wl.E_loc, wl.h, wl.m, dtype=torch.float32, device=dev),
+          torch.empty(wl.E_loc, wl.h, wl.m, dtype=torch.float32, device=dev),
+          torch.empty(wl.E_loc, wl.m, wl.h, dtype=torch.float32, device=dev))
+    bws = torch.empty(G.moe_backward_workspace_bytes(sh, wl.dtype), dtype=torch.uint8, device=dev)
+    evs = [G.HipEvents(G.MOE_BWD_PROFILE_EVENTS, G.BWD_STAGES) for _ in range(args.steps)]
+    wev = G.HipEvents(G.MOE_BWD_PROFILE_EVENTS, G.BWD_STAGES)
+    for _ in range(args.warmup):
+        G.moe_backward_profiled(sh, wl.dtype, x, dy, saved, pbwd, wev, dx=dx, dw=dw, ws=bws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs:
+        G.moe_backward_profiled(sh, wl.dtype, x, dy, saved, pbwd, ev, dx=dx, dw=dw, ws=bws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stages = {k: 0.0 for k in G.BWD_STAGES}
+    for ev in evs:
+        for k, v in ev.stage_ms().items():
+            stages[k] += v / args.steps
+    for ev in evs + [wev]:
+        ev.close()
+    R = wl.T * wl.k
+    flops = 12.0 * R * wl.h * wl.m  # dH, dA (dgrad) and the three weight gradients
+    peak = PEAK_TFLOPS[wl.dtype]
+    gemm_ms = sum(stages[k] for k in ("dgrad_dh_dswiglu", "dgrad_da", "wgrad_gate_up",
+                                       "wgrad_down"))
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "gemm_mfma_frac": round(flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+            "flop": flops, "dw_dtype": "f32", "training_forward_ms": round(fwd_saved_ms, 4),
+            "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
+
+
 def main() -> int:
     args = parse()
     if args.copy_calibration:
@@ -218,6 +270,10 @@ def main() -> int:
         ms = stages[name]
         return round(by[name] / (ms * 1e-3) / 1e9, 1) if ms > 0 and by[name] else None
 
+    backward = None
+    if wl.backward and not args.no_backward:
+        backward = time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args)
+
     baseline = None
     if args.cpu_sample_tokens > 0:
         def host_bits(t):
@@ -264,6 +320,8 @@ def main() -> int:
         "stages_gbs": {k: gbs(k) for k in ("gather", "combine", "topk")},
         "cpu_baseline": baseline,
     }
+    if backward is not None:
+        out["backward"] = backward
     print(json.dumps(out), flush=True)
     return 0
 
