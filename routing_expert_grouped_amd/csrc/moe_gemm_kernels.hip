@@ -441,25 +441,54 @@ __device__ __forceinline__ void lds_barrier() {
 #ifndef MOE_BIG_NS_MX
 #define MOE_BIG_NS_MX 3
 #endif
+// routed-row ring depth: one stage deeper than the weight ring (the routed rows miss L2 more:
+// every XCD streams all of a band's row panels but only its own weight panels)
+#ifndef MOE_BIG_NSR_BF16
+#define MOE_BIG_NSR_BF16 3
+#endif
+#ifndef MOE_BIG_NSR_BF16_128
+#define MOE_BIG_NSR_BF16_128 4
+#endif
+#ifndef MOE_BIG_NSR_MX
+#define MOE_BIG_NSR_MX 4
+#endif
 
-template <int MODE, bool MX, int BM, int RB, int NS>
+template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   constexpr int BN = kBigBN;
   constexpr int ROWS = BN + BM;
-  constexpr int STAGE = ROWS * RB;
+  constexpr int WSTAGE = BN * RB;                // one stage of the weight operand
+  constexpr int RSTAGE = BM * RB;                // one stage of the routed rows
   constexpr int NI = 4;                          // weight fragments per wave
   constexpr int NJ = BM / 64;                    // row fragments per wave
   constexpr int LOADS = ROWS * RB / 16 / 256;    // 16-byte DMA loads per thread per stage
   constexpr int SLOTS = RB / 16;
+  constexpr int QW = BN * SLOTS / 256;           // of which weight rows
+  constexpr int QR = LOADS - QW;                 // and routed rows
   constexpr int SPS = MX ? RB / 64 : RB / 32;    // MFMA k-steps per stage
   constexpr int PC = MX ? 4 / SPS : 1;           // stages per 256-element MX chunk
   constexpr int NSC = MX ? NI + NJ : 0;          // scale loads per chunk
-  constexpr int MAXN = LOADS * (NS - 2);
-  static_assert(MAXN < 64 && NS <= 5, "vmcnt range");
+  // a barrier point's loads go out in SPS parts of D, one per k-step of the next stage (the last
+  // part after the following barrier), so the DMA load is spread over the stage; the last part
+  // holds WL weight and RL routed-row units
+  constexpr int D = LOADS / SPS;
+  constexpr int U0 = (SPS - 1) * D;
+  constexpr int WL = QW > U0 ? QW - U0 : 0;
+  constexpr int RL = LOADS - (U0 > QW ? U0 : QW);
+  // loads a wave has in flight after the later of its two groups of a stage (see wait_stage),
+  // in the steady state
+  constexpr int NFULL = NSR > NS ? QR * (NS - 1) + QW * (NS - 2) : LOADS * (NS - 2);
+  constexpr int NSTEADY = NFULL - WL - RL;
+  static_assert(LOADS % SPS == 0 && NSTEADY >= 0, "DMA parts per k-step");
+  static_assert(NSR == NS || NSR == NS + 1, "row ring as deep as the weight ring or one deeper");
+  static_assert(NFULL < 64 && NS >= 2 && NS <= 5, "vmcnt range");
   static_assert(!MX || PC >= 2, "the scale prefetch needs two stages per chunk");
   static_assert(MX || SPS % 2 == 0, "fragment double buffer alternates within a stage");
-  static_assert(NS * STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
+  static_assert(NS * WSTAGE + NSR * RSTAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * WSTAGE + NSR * RSTAGE];
+  // stage s: weight rows in ring slot s % NS, routed rows in ring slot s % NSR
+  auto wbuf = [&](int s) { return lds + (s % NS) * WSTAGE; };
+  auto rbuf = [&](int s) { return lds + NS * WSTAGE + (s % NSR) * RSTAGE; };
 
   // ---- which tile: band b of band_m M tiles, XCD x takes the x-th eighth of it (N-major)
   const int mt_total = MODE == kEpiWgrad ? p.tiles_total : *p.tile_count;
@@ -503,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
   const int wn = wave >> 1;
   const int wm = wave & 1;
   const int li = lane & 31;
@@ -532,10 +561,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   }
   const size_t ldk = (size_t)Kt * EL;
 
-  // ---- DMA sources: unit id = q * 256 + tid lands at stage byte id * 16 = LDS row id / SLOTS,
-  //      physical slot id % SLOTS, and must carry logical chunk slot ^ f(row). Units q < QW are
-  //      weight rows, the rest routed rows; 32-bit offsets from the two (uniform) bases.
-  constexpr int QW = BN * SLOTS / 256;
+  // ---- DMA sources: unit id = q * 256 + tid is LDS row id / SLOTS (rows BN.. are the routed
+  //      rows, at row id / SLOTS - BN of their ring slot), physical slot id % SLOTS, and must carry
+  //      logical chunk slot ^ f(row) (f(BN + r) = f(r) for BN = 256). Units q < QW are weight
+  //      rows, the rest routed rows; 32-bit offsets from the two (uniform) bases.
   uint32_t src[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
@@ -555,11 +584,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   auto stage_off = [&](int j) -> size_t { return (size_t)RB * j; };
   const int nk = (int)(ldk / RB);
   const int nchunks = MX ? nk / PC : 0;
-  auto issue = [&](int j) {
-    const uint32_t off = (uint32_t)stage_off(j);
-    uint8_t* b = lds + (j % NS) * STAGE + wave * 1024;
+  // part `part` (units [part D, part D + D)) of barrier point b's groups W(b+NS-1), R(b+NSR-1),
+  // skipping stages that do not exist; they go to the ring slots of stage b-1
+  auto issue_part = [&](int b, int part) {
+    const int sw = b + NS - 1, sr = b + NSR - 1;
+    const bool hw = sw >= 0 && sw < nk, hr = sr >= 0 && sr < nk;
+    const uint32_t offw = (uint32_t)stage_off(sw), offr = (uint32_t)stage_off(sr);
+    uint8_t* bw = wbuf(sw < 0 ? 0 : sw) + wave * 1024;
+    uint8_t* br = rbuf(sr < 0 ? 0 : sr) + wave * 1024;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) dma16((q < QW ? wexp : rows_b) + (src[q] + off), b + q * 4096);
+    for (int q = 0; q < LOADS; ++q) {
+      if (q / D != part) continue;
+      if (q < QW) {
+        if (hw) dma16(wexp + (src[q] + offw), bw + q * 4096);
+      } else {
+        if (hr) dma16(rows_b + (src[q] + offr), br + (q - QW) * 4096);
+      }
+    }
   };
 
   // ---- MX scale words. In K order, MFMA step s of a 256-element chunk multiplies blocks 2s (its
@@ -592,24 +633,39 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     for (int j = 0; j < NJ; ++j) r[j] = scale_word(rsb, sr_off[j], cc);
   };
 
-  // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact):
-  //   prologue: S(0), G(0) .. G(NS-2); barrier point j = 0 .. nk-1: wait for G(j), barrier,
-  //   G(j+NS-1) if it exists, then S(cc+1) when j = cc * PC + 1 and chunk cc+1 exists.
-  // When point j waits, the groups issued after G(j) are G(j+1 .. min(j+NS-2, nk-1)); waiting
-  // for vmcnt(LOADS * that many) completes G(j). Scale loads issued after G(j) are not counted,
-  // which only makes the wait stricter (they complete too), never too weak.
-  auto wait_stage = [&](int j) {
-    const int ng = min(j + NS - 2, nk - 1) - j;
-    asm volatile("" ::: "memory");
-    if (ng >= 3 && NS >= 5) wait_vmcnt<LOADS * (NS >= 5 ? 3 : 0)>();
-    else if (ng >= 2 && NS >= 4) wait_vmcnt<LOADS * (NS >= 4 ? 2 : 0)>();
-    else if (ng >= 1 && NS >= 3) wait_vmcnt<LOADS * (NS >= 3 ? 1 : 0)>();
-    else wait_vmcnt<0>();
+  // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact).
+  //   Barrier point b's groups are W(b+NS-1) then R(b+NSR-1) (those that exist), as units
+  //   0 .. LOADS-1, weight units first. The prologue issues S(0) and all groups of the points
+  //   b = -(NSR-1) .. -1. Stage j then issues part t of point j's groups in its k-step t, the
+  //   last part right after barrier point j+1, followed by S(cc+1) when j+1 = cc * PC + 1 and
+  //   chunk cc+1 exists.
+  //   Loads complete in issue order, so point j, which needs W(j) and R(j), waits until only the
+  //   loads issued after the later of the two are left. With every group of the points before j
+  //   issued, those would be:
+  //     NSR == NS + 1: W(j) is later; after it come R(j+1 .. j+NS-1) and W(j+1 .. j+NS-2);
+  //     NSR == NS:     R(j) is later; after it come W and R of j+1 .. j+NS-2;
+  //   each only if that stage exists (< nk); the last part of point j-1 is not issued yet, so
+  //   its units are taken off. Scale loads issued after them are not counted, which only makes
+  //   the wait stricter (they complete too), never too weak.
+  auto last_part = [&](int b) {
+    return (b + NS - 1 >= 0 && b + NS - 1 < nk ? WL : 0) +
+           (b + NSR - 1 >= 0 && b + NSR - 1 < nk ? RL : 0);
   };
+  auto wait_stage = [&](int j) {
+    const int nw = max(0, min(j + NS - 2, nk - 1) - j);  // stages j+1 .. j+NS-2 that exist
+    int n;
+    if constexpr (NSR > NS) n = QR * max(0, min(j + NS - 1, nk - 1) - j) + QW * nw;
+    else n = LOADS * nw;
+    if (j >= 1) n -= last_part(j - 1);
+    asm volatile("" ::: "memory");
+    wait_vmcnt_range<0, NFULL>(n);
+  };
+  // barrier point j: stage j is in LDS for every wave and stage j-1 read by every wave; then the
+  // last part of point j-1's loads and the scale words of the next chunk
   auto barrier_point = [&](int j) {
     wait_stage(j);
     lds_barrier();
-    if (j + NS - 1 < nk) issue(j + NS - 1);
+    if (j >= 1) issue_part(j - 1, SPS - 1);
     if constexpr (MX) {
       if (j % PC == 1 && j / PC + 1 < nchunks) sload(j / PC + 1, nscw, nscr);
     }
@@ -624,8 +680,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = BN + (BM / 2) * wm + 32 * j + li;
-    fbr[j] = row * RB + 16 * big_swz<RB>(row);
+    const int row = (BM / 2) * wm + 32 * j + li;  // within the routed-row ring slot
+    fbr[j] = row * RB + 16 * big_swz<RB>(BN + row);
   }
 
   using FragT = typename std::conditional<MX, i32x8_t, bf16x8_t>::type;
@@ -634,18 +690,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     FragT r[NJ];
   };
   constexpr int NR = (MX ? 2 : 1) * (NI + NJ);  // 16-byte LDS reads per k-step
-  // 16-byte piece `idx` (0 .. NR-1) of the fragments of k-step t from stage buffer b; weight
-  // fragments first, each MX fragment being two pieces (its two half blocks)
-  auto load_piece = [&](Frags& F, const uint8_t* b, int t, int idx) {
+  // 16-byte piece `idx` (0 .. NR-1) of the fragments of k-step t from the stage's weight ring
+  // slot bw and routed-row ring slot br; weight fragments first, each MX fragment being two
+  // pieces (its two half blocks)
+  auto load_piece = [&](Frags& F, const uint8_t* bw, const uint8_t* br, int t, int idx) {
     if constexpr (!MX) {
       const int c = 16 * (2 * t + g);
-      if (idx < NI) F.w[idx] = *reinterpret_cast<const bf16x8_t*>(b + (fbw[idx] ^ c));
-      else F.r[idx - NI] = *reinterpret_cast<const bf16x8_t*>(b + (fbr[idx - NI] ^ c));
+      if (idx < NI) F.w[idx] = *reinterpret_cast<const bf16x8_t*>(bw + (fbw[idx] ^ c));
+      else F.r[idx - NI] = *reinterpret_cast<const bf16x8_t*>(br + (fbr[idx - NI] ^ c));
     } else {
       // MFMA step t of the stage: bytes 0-15 of lane (i, g) are K [64t + 16g, +16) (first block),
       // bytes 16-31 are K [64t + 32 + 16g, +16) (second block)
       const int f = idx >> 1, half = idx & 1;
       const int c = 16 * (4 * t + 2 * half + g);
+      const uint8_t* b = f < NI ? bw : br;
       const int fb = f < NI ? fbw[f] : fbr[f - NI];
       const i32x4_t v = *reinterpret_cast<const i32x4_t*>(b + (fb ^ c));
       FragT& dst = f < NI ? F.w[f] : F.r[f - NI];
@@ -653,9 +711,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       for (int q = 0; q < 4; ++q) dst[4 * half + q] = v[q];
     }
   };
-  auto load_frags = [&](Frags& F, const uint8_t* b, int t) {
+  auto load_frags = [&](Frags& F, int j, int t) {  // k-step t of stage j
 #pragma unroll
-    for (int idx = 0; idx < NR; ++idx) load_piece(F, b, t, idx);
+    for (int idx = 0; idx < NR; ++idx) load_piece(F, wbuf(j), rbuf(j), t, idx);
   };
 
   f32x16_t acc[NI][NJ];
@@ -683,35 +741,40 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   if (MODE != kEpiWgrad || nk > 0) {
   if constexpr (MX) sload(0, scw, scr);
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
+  for (int b = -(NSR - 1); b < 0; ++b)
+#pragma unroll
+    for (int part = 0; part < SPS; ++part) issue_part(b, part);
   barrier_point(0);
-  load_frags(FA, lds, 0);
+  load_frags(FA, 0, 0);
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
 
-  // ---- steady-state k-step (stage j with j + NS < nk, so every wait and load is unconditional):
+  // ---- steady-state k-step (stage j with j + NSR < nk, so every wait and load is unconditional):
   // its MFMAs interleaved one by one with the other work, in a fixed order the compiler may not
-  // change (sched_barrier): the next k-step's LDS reads, and in a stage's last k-step, right
-  // after the first MFMA, the barrier point of stage j+1 followed by the DMA of stage j+NS, the
-  // next chunk's MX scale words and the reads of stage j+1's first fragments.
+  // change (sched_barrier): part t of barrier point j's DMA (into stage j-1's ring slots), the
+  // next k-step's LDS reads, and in a stage's last k-step, right after the first MFMA, the wait
+  // and barrier of point j+1 followed by the last DMA part, the next chunk's MX scale words and
+  // the reads of stage j+1's first fragments.
   auto kstep_fast = [&](int j, auto t_tag, auto p_tag, Frags& cur, Frags& nxt) {
     constexpr int t = decltype(t_tag)::value;
     constexpr int P = decltype(p_tag)::value;
     constexpr bool LAST = t + 1 == SPS;
     constexpr bool SCALES = MX && LAST && P == 0;  // barrier point j+1 = cc * PC + 1
-    constexpr int NDMA = LAST ? LOADS : 0;
+    constexpr int NDMA = D;
     constexpr int NSCL = SCALES ? NSC : 0;
     constexpr int NOPS = NDMA + NSCL + NR;
     constexpr int SLOTS_M = NM - 2;  // leave the last two MFMAs to cover the last reads
     constexpr int K = (NOPS + SLOTS_M - 1) / SLOTS_M;
-    const uint8_t* rb = LAST ? lds + ((j + 1) % NS) * STAGE : lds + (j % NS) * STAGE;
+    const uint8_t* rbw = LAST ? wbuf(j + 1) : wbuf(j);
+    const uint8_t* rbr = LAST ? rbuf(j + 1) : rbuf(j);
     const int rt = LAST ? 0 : t + 1;
-    const uint32_t doff = (uint32_t)stage_off(j + NS);
-    uint8_t* db = lds + (j % NS) * STAGE + wave * 1024;  // stage j's buffer, read completely
+    const uint32_t doffw = (uint32_t)stage_off(j + NS - 1);  // point j's groups
+    const uint32_t doffr = (uint32_t)stage_off(j + NSR - 1);
+    uint8_t* dbw = wbuf(j + NS - 1) + wave * 1024;  // stage j-1's ring slots
+    uint8_t* dbr = rbuf(j + NSR - 1) + wave * 1024;
     const int cc_next = min(j / PC + 1, nchunks - 1);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -719,7 +782,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (LAST) {
         if (m == 0) {
-          wait_vmcnt_fenced<LOADS * (NS - 2)>();
+          wait_vmcnt_fenced<NSTEADY>();
           lds_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -729,7 +792,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
         const int op = (m - 1) * K + o;
         if (m >= 1 && op < NOPS) {
           if (op < NDMA) {
-            dma16((op < QW ? wexp : rows_b) + (src[op] + doff), db + op * 4096);
+            const int q = t * D + op;
+            if (q < QW) dma16(wexp + (src[q] + doffw), dbw + q * 4096);
+            else dma16(rows_b + (src[q] + doffr), dbr + (q - QW) * 4096);
           } else if (op < NDMA + NSCL) {
             const int k = op - NDMA;
             if constexpr (MX) {
@@ -737,7 +802,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
               else nscr[k - NI] = scale_word(rsb, sr_off[k - NI], cc_next);
             }
           } else {
-            load_piece(nxt, rb, rt, op - NDMA - NSCL);
+            load_piece(nxt, rbw, rbr, rt, op - NDMA - NSCL);
           }
         }
       }
@@ -750,11 +815,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     constexpr int t = decltype(t_tag)::value;
     constexpr int P = decltype(p_tag)::value;
     if constexpr (t + 1 < SPS) {
-      load_frags(nxt, lds + (j % NS) * STAGE, t + 1);
+      issue_part(j, t);
+      load_frags(nxt, j, t + 1);
     } else {
-      if (j + 1 < nk) {
+      if (j + 1 < nk) {  // (the last stage's point has no groups left to issue)
         barrier_point(j + 1);
-        load_frags(nxt, lds + ((j + 1) % NS) * STAGE, 0);
+        load_frags(nxt, j + 1, 0);
       }
     }
     mfmas(cur, P * SPS + t);
@@ -807,8 +873,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       for (int j = j0; j < j1; ++j) stage(j, I0{}, fast_tag, FA, FB);
     }
   };
-  // steady state: stages j with j + NS < nk (rounded down to whole MX chunks), then the rest
-  const int jsteady = max(0, (nk - NS) / PC * PC);
+  // steady state: stages j with j + NSR < nk (rounded down to whole MX chunks), then the rest
+  const int jsteady = max(0, (nk - NSR) / PC * PC);
   run(0, jsteady, std::true_type{});
   run(jsteady, nk, std::false_type{});
   }  // nk > 0
@@ -1205,7 +1271,10 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
                                               (MXV ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16),          \
                                               (MXV ? MOE_BIG_NS_MX                              \
                                                    : (BMV == 128 ? MOE_BIG_NS_BF16_128          \
-                                                                 : MOE_BIG_NS_BF16))>),         \
+                                                                 : MOE_BIG_NS_BF16)),           \
+                                              (MXV ? MOE_BIG_NSR_MX                             \
+                                                   : (BMV == 128 ? MOE_BIG_NSR_BF16_128         \
+                                                                 : MOE_BIG_NSR_BF16))>),        \
                      G, dim3(256), 0, st, A)
 
 // grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most
