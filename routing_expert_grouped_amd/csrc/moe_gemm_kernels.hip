@@ -425,33 +425,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// stage width and depth per precision (LDS: NS * (256 + BM) * RB bytes, at most 160 KB)
-#ifndef MOE_BIG_RB_BF16
-#define MOE_BIG_RB_BF16 128
-#endif
-#ifndef MOE_BIG_NS_BF16
-#define MOE_BIG_NS_BF16 2
-#endif
-#ifndef MOE_BIG_NS_BF16_128
-#define MOE_BIG_NS_BF16_128 3  // 128-row BF16 tiles: 3 stages of 48 KB
-#endif
-#ifndef MOE_BIG_RB_MX
-#define MOE_BIG_RB_MX 128
-#endif
-#ifndef MOE_BIG_NS_MX
-#define MOE_BIG_NS_MX 3
-#endif
-// routed-row ring depth: one stage deeper than the weight ring (the routed rows miss L2 more:
-// every XCD streams all of a band's row panels but only its own weight panels)
-#ifndef MOE_BIG_NSR_BF16
-#define MOE_BIG_NSR_BF16 3
-#endif
-#ifndef MOE_BIG_NSR_BF16_128
-#define MOE_BIG_NSR_BF16_128 4
-#endif
-#ifndef MOE_BIG_NSR_MX
-#define MOE_BIG_NSR_MX 4
-#endif
+// K bytes per stage (whole 128-byte lines) and ring depths per tile height. LDS per workgroup:
+// (NS * 256 + NSR * BM) * 128 bytes, at most 160 KB: BM = 256 and 192 take a two-deep weight ring
+// and a three-deep row ring (160 KB, 136 KB), BM = 128 three and four (160 KB). The routed-row
+// ring is one stage deeper: those panels miss L2 more (every XCD streams all of a band's row
+// panels but only its own weight panels).
+constexpr int kBigRB = 128;
+__host__ __device__ constexpr int big_ns(int bm) { return bm >= 192 ? 2 : 3; }
+__host__ __device__ constexpr int big_nsr(int bm) { return big_ns(bm) + 1; }
 
 template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
@@ -468,18 +449,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   constexpr int SPS = MX ? RB / 64 : RB / 32;    // MFMA k-steps per stage
   constexpr int PC = MX ? 4 / SPS : 1;           // stages per 256-element MX chunk
   constexpr int NSC = MX ? NI + NJ : 0;          // scale loads per chunk
-  // a barrier point's loads go out in SPS parts of D, one per k-step of the next stage (the last
-  // part after the following barrier), so the DMA load is spread over the stage; the last part
-  // holds WL weight and RL routed-row units
-  constexpr int D = LOADS / SPS;
-  constexpr int U0 = (SPS - 1) * D;
+  // a barrier point's loads go out in SPS parts, one per k-step of the next stage (the last part
+  // after the following barrier), so the DMA load is spread over the stage. The last part starts
+  // at unit U0, after every weight unit when the weight ring is two deep (its group is needed at
+  // the following barrier), and holds WL weight and RL routed-row units; the other parts split
+  // [0, U0) evenly.
+  constexpr int U0a = (SPS - 1) * (LOADS / SPS);
+  constexpr int U0 = NS == 2 && QW > U0a ? QW : U0a;
   constexpr int WL = QW > U0 ? QW - U0 : 0;
   constexpr int RL = LOADS - (U0 > QW ? U0 : QW);
   // loads a wave has in flight after the later of its two groups of a stage (see wait_stage),
   // in the steady state
   constexpr int NFULL = NSR > NS ? QR * (NS - 1) + QW * (NS - 2) : LOADS * (NS - 2);
   constexpr int NSTEADY = NFULL - WL - RL;
-  static_assert(LOADS % SPS == 0 && NSTEADY >= 0, "DMA parts per k-step");
+  static_assert(SPS >= 2 && NSTEADY >= 0 && (NS > 2 || WL == 0), "DMA parts per k-step");
   static_assert(NSR == NS || NSR == NS + 1, "row ring as deep as the weight ring or one deeper");
   static_assert(NFULL < 64 && NS >= 2 && NS <= 5, "vmcnt range");
   static_assert(!MX || PC >= 2, "the scale prefetch needs two stages per chunk");
@@ -584,17 +567,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   auto stage_off = [&](int j) -> size_t { return (size_t)RB * j; };
   const int nk = (int)(ldk / RB);
   const int nchunks = MX ? nk / PC : 0;
-  // part `part` (units [part D, part D + D)) of barrier point b's groups W(b+NS-1), R(b+NSR-1),
-  // skipping stages that do not exist; they go to the ring slots of stage b-1
+  // first unit of part t (t = SPS: the end)
+  auto part_start = [](int t) { return t >= SPS ? LOADS : t * U0 / (SPS - 1); };
+  // part `part` of barrier point b's groups W(b+NS-1), R(b+NSR-1), skipping stages that do not
+  // exist; they go to the ring slots of stage b-1
   auto issue_part = [&](int b, int part) {
     const int sw = b + NS - 1, sr = b + NSR - 1;
     const bool hw = sw >= 0 && sw < nk, hr = sr >= 0 && sr < nk;
     const uint32_t offw = (uint32_t)stage_off(sw), offr = (uint32_t)stage_off(sr);
     uint8_t* bw = wbuf(sw < 0 ? 0 : sw) + wave * 1024;
     uint8_t* br = rbuf(sr < 0 ? 0 : sr) + wave * 1024;
+    const int q0 = part_start(part), q1 = part_start(part + 1);
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
-      if (q / D != part) continue;
+      if (q < q0 || q >= q1) continue;
       if (q < QW) {
         if (hw) dma16(wexp + (src[q] + offw), bw + q * 4096);
       } else {
@@ -763,7 +749,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     constexpr int P = decltype(p_tag)::value;
     constexpr bool LAST = t + 1 == SPS;
     constexpr bool SCALES = MX && LAST && P == 0;  // barrier point j+1 = cc * PC + 1
-    constexpr int NDMA = D;
+    constexpr int Q0 = t * U0 / (SPS - 1);  // this k-step's DMA part: units [Q0, Q0 + NDMA)
+    constexpr int NDMA = (t + 1 == SPS ? LOADS : (t + 1) * U0 / (SPS - 1)) - Q0;
     constexpr int NSCL = SCALES ? NSC : 0;
     constexpr int NOPS = NDMA + NSCL + NR;
     constexpr int SLOTS_M = NM - 2;  // leave the last two MFMAs to cover the last reads
@@ -792,7 +779,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
         const int op = (m - 1) * K + o;
         if (m >= 1 && op < NOPS) {
           if (op < NDMA) {
-            const int q = t * D + op;
+            const int q = Q0 + op;
             if (q < QW) dma16(wexp + (src[q] + doffw), dbw + q * 4096);
             else dma16(rows_b + (src[q] + doffr), dbr + (q - QW) * 4096);
           } else if (op < NDMA + NSCL) {
@@ -1195,11 +1182,14 @@ struct FfnLayout {
   int max_tiles;
 };
 
-// rows per M tile: the large-tile kernel (h % 256 == 0, m % 128 == 0) takes 256 rows when the
-// experts hold 224 rows or more on average, else 128; the small-tile kernel always 128
+// rows per M tile: the large-tile kernel (h % 256 == 0, m % 128 == 0) takes 256 rows (BF16) when
+// the experts hold 224 rows or more on average, 192 rows (MXFP8) from 128 rows on average, else
+// 128; the small-tile kernel always 128
 int ffn_tile_rows(int R, int h, int m, int E_loc, bool mx) {
   if (h % kBigBN || (2 * m) % kBigBN) return kBM;
-  if (mx) return 128;  // the 256-row MXFP8 tile does not fit the register file
+  // MXFP8: a 256-row tile does not fit the register file; 192 rows (three 32-row fragments per
+  // wave) does, and wastes less on experts of a few hundred rows than two 128-row tiles
+  if (mx) return (R / E_loc >= 128) ? 192 : 128;
   return (R / E_loc >= 224) ? 256 : 128;
 }
 bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
@@ -1267,14 +1257,8 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
 // kernels launched by name in non-template functions, so that each instantiation is compiled for
 // the device
 #define MOE_BIG(MODEV, MXV, BMV, G, A)                                                          \
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV,                                  \
-                                              (MXV ? MOE_BIG_RB_MX : MOE_BIG_RB_BF16),          \
-                                              (MXV ? MOE_BIG_NS_MX                              \
-                                                   : (BMV == 128 ? MOE_BIG_NS_BF16_128          \
-                                                                 : MOE_BIG_NS_BF16)),           \
-                                              (MXV ? MOE_BIG_NSR_MX                             \
-                                                   : (BMV == 128 ? MOE_BIG_NSR_BF16_128         \
-                                                                 : MOE_BIG_NSR_BF16))>),        \
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV, kBigRB, big_ns(BMV),             \
+                                              big_nsr(BMV)>),                                   \
                      G, dim3(256), 0, st, A)
 
 // grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most
@@ -1338,7 +1322,11 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   if (big) {
     const dim3 g1 = big_grid(max_tiles, (2 * m) / kBigBN);
     const dim3 g2 = big_grid(max_tiles, h / kBigBN);
-    if (mx) {  // MXFP8 always takes 128-row tiles
+    if (mx && bm == 192) {  // never with save
+      MOE_BIG(kEpiSwiglu, true, 192, g1, a1);
+      if (ev) (void)hipEventRecord(ev[1], st);
+      MOE_BIG(kEpiStore, true, 192, g2, a2);
+    } else if (mx) {
       if (save) MOE_BIG(kEpiSwigluSave, true, 128, g1, a1);
       else MOE_BIG(kEpiSwiglu, true, 128, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
