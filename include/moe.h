@@ -77,9 +77,11 @@ int moe_abi_version(void);
  *              interleaved in blocks of 32: rows 64c..64c+31 are gate columns 32c..32c+31,
  *              rows 64c+32..64c+63 the up columns of the same range), then W2[e][h][m] bf16
  *              (W_down transposed).
- *   MOE_MXFP8: the same two matrices as E4M3 codes, each followed by its E8M0 scales
- *              ([e][2m][h/32] and [e][h][m/32]): blocks of 32 run along h for W1 and along m for
- *              W2, i.e. along each GEMM's reduction axis.
+ *   MOE_MXFP8: the same two matrices as E4M3 codes, each followed by its E8M0 scales; blocks
+ *              of 32 run along h for W1 and along m for W2, i.e. along each GEMM's reduction
+ *              axis, and the scales are stored chunk-major: [e][h/256][2m][8] and
+ *              [e][m/256][h][8], the 8 block scales of one 256-element chunk of a row side by
+ *              side (so a tile's scale words for one chunk are a few cache lines).
  * The shared expert is prepared with the same call, shape.E_loc = 1, shape.m = m_shared, MOE_BF16.
  * ------------------------------------------------------------------------------------------- */
 size_t moe_prepared_weight_bytes(const moe_shape* s, moe_dtype dt);

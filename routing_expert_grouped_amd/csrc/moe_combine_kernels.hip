@@ -11,20 +11,28 @@
 namespace moe {
 namespace {
 
+// KMAX: a bound on k known at compile time, so that the k row loads of a vector are all issued
+// before the first fma (a dropped slot loads a valid row and skips its fma).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ out_rows,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w,
                                                       const uint16_t* __restrict__ shared_out,
                                                       uint16_t* __restrict__ y, int h, int k) {
   const int t = blockIdx.x;
-  int src[16];
-  float wt[16];
-  for (int j = 0; j < k; ++j) {
-    src[j] = inv[(size_t)t * k + j];
-    wt[j] = w ? w[(size_t)t * k + j] : 1.0f;  // fma(1, o, acc) is the plain sum
+  int src[KMAX];
+  float wt[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    src[j] = j < k ? inv[(size_t)t * k + j] : -1;
+    wt[j] = j < k ? (w ? w[(size_t)t * k + j] : 1.0f) : 0.0f;  // fma(1, o, acc) is the plain sum
   }
   const int nv = h / 8;
   for (int v = threadIdx.x; v < nv; v += 256) {
+    uint4 o[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) o[j] = reinterpret_cast<const uint4*>(out_rows + (size_t)max(src[j], 0) * h)[v];
     float acc[8];
     if (shared_out) {
       const uint4 s = reinterpret_cast<const uint4*>(shared_out + (size_t)t * h)[v];
@@ -34,11 +42,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      if (src[j] < 0) continue;  // a dropped assignment contributes nothing
-      const uint4 o = reinterpret_cast<const uint4*>(out_rows + (size_t)src[j] * h)[v];
-      const float of[8] = {bf16_lo(o.x), bf16_hi(o.x), bf16_lo(o.y), bf16_hi(o.y),
-                           bf16_lo(o.z), bf16_hi(o.z), bf16_lo(o.w), bf16_hi(o.w)};
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k || src[j] < 0) continue;  // a dropped assignment contributes nothing
+      const float of[8] = {bf16_lo(o[j].x), bf16_hi(o[j].x), bf16_lo(o[j].y), bf16_hi(o[j].y),
+                           bf16_lo(o[j].z), bf16_hi(o[j].z), bf16_lo(o[j].w), bf16_hi(o[j].w)};
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wt[j], of[q], acc[q]);
     }
@@ -56,8 +64,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,
                           const uint16_t* shared_out, uint16_t* y, int T, int h, int k,
                           hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, st, out_rows, inv, w, shared_out, y,
-                     h, k);
+  if (k <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(256), 0, st, out_rows, inv, w, shared_out,
+                       y, h, k);
+  else
+    hipLaunchKernelGGL(combine_kernel<16>, dim3(T), dim3(256), 0, st, out_rows, inv, w,
+                       shared_out, y, h, k);
   return hipGetLastError();
 }
 

@@ -67,6 +67,14 @@ struct GemmArgs {
   int split_gate_up;            // kEpiWgrad: N is the gate/up-interleaved index (out, out2)
   int out_f32;                  // kEpiWgrad: float32 outputs (else bf16)
   void* out2;                   // kEpiWgrad with split_gate_up: the up half
+  // large-tile kernel, MX scale layouts: 0 = natural [rows][K/32]; 1 = chunk-major
+  // [K/256][rows][8] (the 8 scale bytes of one 256-element chunk of every row side by side, so a
+  // wave's scale words of a chunk are a few cache lines). Weights: rows = N per expert; routed
+  // rows (input and the H scales GEMM-1 writes): rows = sc_rows.
+  int w_sc_cm;
+  int r_sc_cm;
+  int out_sc_cm;
+  int sc_rows;
 };
 
 // Epilogue (and grouping) modes of the large-tile kernel.
@@ -417,6 +425,17 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
 #endif
 }
 
+// A 64-bit vector load the compiler does not track: it puts no wait of its own before the value's
+// first use (it would wait for every LDS DMA load issued before, as it cannot count those), so the
+// caller must have waited for it with the vmcnt of a later load. Host pass: never called.
+__device__ __forceinline__ uint64_t load_dwordx2_untracked(const uint8_t* base, uint32_t off) {
+  uint64_t v = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx2 %0, %1, %2" : "=v"(v) : "v"(off), "s"(base));
+#endif
+  return v;
+}
+
 // every LDS read of this wave has returned, then all waves meet; no memory access moves across
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -465,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   static_assert(SPS >= 2 && NSTEADY >= 0 && (NS > 2 || WL == 0), "DMA parts per k-step");
   static_assert(NSR == NS || NSR == NS + 1, "row ring as deep as the weight ring or one deeper");
   static_assert(NFULL < 64 && NS >= 2 && NS <= 5, "vmcnt range");
-  static_assert(!MX || PC >= 2, "the scale prefetch needs two stages per chunk");
+  static_assert(!MX || PC == 2, "an MX chunk of 256 elements is two stages");
   static_assert(MX || SPS % 2 == 0, "fragment double buffer alternates within a stage");
   static_assert(NS * WSTAGE + NSR * RSTAGE <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NS * WSTAGE + NSR * RSTAGE];
@@ -591,32 +610,49 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 
   // ---- MX scale words. In K order, MFMA step s of a 256-element chunk multiplies blocks 2s (its
   //      first block, scale from lane group 0) and 2s+1 (second block, lane group 1), so lane group
-  //      g needs the scale bytes of blocks g, 2+g, 4+g, 6+g of the chunk: one 8-byte load of the
-  //      row's chunk scales and a byte permute give that word, and the MFMA's byte select picks
-  //      step s. 32-bit offsets from the expert's and the rows' scale bases.
+  //      g needs the scale bytes of blocks g, 2+g, 4+g, 6+g of the chunk: the row's 8 chunk scale
+  //      bytes are loaded a chunk ahead and byte-permuted into that word once the chunk's first
+  //      barrier point has waited for them; the MFMA's byte select picks step s. 32-bit offsets
+  //      from the expert's and the rows' scale bases.
   uint32_t sw_off[NI], sr_off[NJ];
-  int scw[NI], scr[NJ], nscw[NI], nscr[NJ];
+  int scw[NI], scr[NJ];
+  uint64_t nscw[NI], nscr[NJ];
   const uint32_t perm_sel = g ? 0x07050301u : 0x06040200u;  // bytes g, 2+g of lo, g, 2+g of hi
+  // byte offsets: row (or weight row) x, chunk cc at x * *_rs + cc * *_cs
+  uint32_t w_cs = 8, r_cs = 8;
   if constexpr (MX) {
     const uint32_t nsb = (uint32_t)(Kt / kMxBlock);
+    const uint32_t w_rs = p.w_sc_cm ? 8u : nsb, r_rs = p.r_sc_cm ? 8u : nsb;
+    if (p.w_sc_cm) w_cs = 8u * (uint32_t)p.N;
+    if (p.r_sc_cm) r_cs = 8u * (uint32_t)p.sc_rows;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) sw_off[i] = (uint32_t)(n0 + 128 * wn + 32 * i + li) * nsb;
+    for (int i = 0; i < NI; ++i) sw_off[i] = (uint32_t)(n0 + 128 * wn + 32 * i + li) * w_rs;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int r = row0 + (BM / 2) * wm + 32 * j + li;
       r = r < row_end ? r : row_end - 1;
-      sr_off[j] = (uint32_t)r * nsb;
+      sr_off[j] = (uint32_t)r * r_rs;
     }
   }
-  auto scale_word = [&](const uint8_t* base, uint32_t off, int cc) -> int {
-    const uint2 v = *reinterpret_cast<const uint2*>(base + (off + 8 * cc));
-    return (int)__builtin_amdgcn_perm(v.y, v.x, perm_sel);
+  // (issued ahead of a DMA load that the chunk's first barrier point waits for, so that wait
+  // covers them)
+  auto scale_raw = [&](const uint8_t* base, uint32_t off, uint32_t cs, int cc) -> uint64_t {
+    return load_dwordx2_untracked(base, off + cs * (uint32_t)cc);
   };
-  auto sload = [&](int cc, int (&w)[NI], int (&r)[NJ]) {
+  auto scale_word = [&](uint64_t v) -> int {
+    return (int)__builtin_amdgcn_perm((uint32_t)(v >> 32), (uint32_t)v, perm_sel);
+  };
+  auto sload = [&](int cc, uint64_t (&w)[NI], uint64_t (&r)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) w[i] = scale_word(wsb, sw_off[i], cc);
+    for (int i = 0; i < NI; ++i) w[i] = scale_raw(wsb, sw_off[i], w_cs, cc);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) r[j] = scale_word(rsb, sr_off[j], cc);
+    for (int j = 0; j < NJ; ++j) r[j] = scale_raw(rsb, sr_off[j], r_cs, cc);
+  };
+  auto take_scales = [&]() {  // after the wait of the chunk's first barrier point
+#pragma unroll
+    for (int i = 0; i < NI; ++i) scw[i] = scale_word(nscw[i]);
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) scr[q] = scale_word(nscr[q]);
   };
 
   // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact).
@@ -725,12 +761,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   //      stores zeros; the condition is uniform over the workgroup)
   Frags FA, FB;
   if (MODE != kEpiWgrad || nk > 0) {
-  if constexpr (MX) sload(0, scw, scr);
+  if constexpr (MX) {
+    sload(0, nscw, nscr);
+  }
 #pragma unroll
   for (int b = -(NSR - 1); b < 0; ++b)
 #pragma unroll
     for (int part = 0; part < SPS; ++part) issue_part(b, part);
   barrier_point(0);
+  if constexpr (MX) take_scales();
   load_frags(FA, 0, 0);
 
   using I0 = std::integral_constant<int, 0>;
@@ -742,16 +781,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   // its MFMAs interleaved one by one with the other work, in a fixed order the compiler may not
   // change (sched_barrier): part t of barrier point j's DMA (into stage j-1's ring slots), the
   // next k-step's LDS reads, and in a stage's last k-step, right after the first MFMA, the wait
-  // and barrier of point j+1 followed by the last DMA part, the next chunk's MX scale words and
-  // the reads of stage j+1's first fragments.
+  // and barrier of point j+1 followed by the last DMA part and the reads of stage j+1's first
+  // fragments. A chunk's first k-step starts with the next chunk's MX scale words.
   auto kstep_fast = [&](int j, auto t_tag, auto p_tag, Frags& cur, Frags& nxt) {
     constexpr int t = decltype(t_tag)::value;
     constexpr int P = decltype(p_tag)::value;
     constexpr bool LAST = t + 1 == SPS;
-    constexpr bool SCALES = MX && LAST && P == 0;  // barrier point j+1 = cc * PC + 1
+    constexpr bool SCALES = MX && t == 0 && P == 0;  // the first k-step of chunk cc
     constexpr int Q0 = t * U0 / (SPS - 1);  // this k-step's DMA part: units [Q0, Q0 + NDMA)
     constexpr int NDMA = (t + 1 == SPS ? LOADS : (t + 1) * U0 / (SPS - 1)) - Q0;
     constexpr int NSCL = SCALES ? NSC : 0;
+    // the scale words of chunk cc + 1 went out at the start of stage cc * PC = j - P, as the
+    // first loads of that stage; they follow every load of stage j + 1's later group, and so
+    // are in flight beside the NSTEADY loads at point j + 1, when that group's last part went
+    // out at a barrier point up to j - P (which is j + 3 - NS at the latest)
+    constexpr int SCL_AFTER = MX && P <= NS - 3 ? NSC : 0;
     constexpr int NOPS = NDMA + NSCL + NR;
     constexpr int SLOTS_M = NM - 2;  // leave the last two MFMAs to cover the last reads
     constexpr int K = (NOPS + SLOTS_M - 1) / SLOTS_M;
@@ -769,7 +813,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (LAST) {
         if (m == 0) {
-          wait_vmcnt_fenced<NSTEADY>();
+          wait_vmcnt_fenced<NSTEADY + SCL_AFTER>();
           lds_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -778,16 +822,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       for (int o = 0; o < K; ++o) {
         const int op = (m - 1) * K + o;
         if (m >= 1 && op < NOPS) {
-          if (op < NDMA) {
-            const int q = Q0 + op;
+          if (op < NSCL) {
+            if constexpr (MX) {
+              if (op < NI) nscw[op] = scale_raw(wsb, sw_off[op], w_cs, cc_next);
+              else nscr[op - NI] = scale_raw(rsb, sr_off[op - NI], r_cs, cc_next);
+            }
+          } else if (op < NSCL + NDMA) {
+            const int q = Q0 + op - NSCL;
             if (q < QW) dma16(wexp + (src[q] + doffw), dbw + q * 4096);
             else dma16(rows_b + (src[q] + doffr), dbr + (q - QW) * 4096);
-          } else if (op < NDMA + NSCL) {
-            const int k = op - NDMA;
-            if constexpr (MX) {
-              if (k < NI) nscw[k] = scale_word(wsb, sw_off[k], cc_next);
-              else nscr[k - NI] = scale_word(rsb, sr_off[k - NI], cc_next);
-            }
           } else {
             load_piece(nxt, rbw, rbr, rt, op - NDMA - NSCL);
           }
@@ -828,12 +871,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       ks(I3{}, F1, F0);
     }
     if constexpr (MX) {
-      if constexpr (P == PC - 1) {  // the next stage starts a new chunk
-#pragma unroll
-        for (int i = 0; i < NI; ++i) scw[i] = nscw[i];
-#pragma unroll
-        for (int q = 0; q < NJ; ++q) scr[q] = nscr[q];
-      }
+      if constexpr (P == PC - 1) take_scales();  // the next stage starts a new chunk
     }
   };
   // stages [j0, j1) in blocks of PC (MX) or one by one (BF16)
@@ -923,7 +961,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
                                   (e4m3_encode(hv[4 * b4 + 3] * inv) << 24);
               *reinterpret_cast<uint32_t*>(out + b4 * 8 + g * 4) = w4;
             }
-            if (g == 0) p.out_scales[(size_t)r * (Hn / kMxBlock) + (col0 >> 5)] = (uint8_t)(sx + 127);
+            if (g == 0) {
+              const int kb = col0 >> 5;  // MX block along m
+              const size_t so = p.out_sc_cm
+                                    ? ((size_t)(kb >> 3) * p.sc_rows + r) * 8 + (kb & 7)
+                                    : (size_t)r * (Hn / kMxBlock) + kb;
+              p.out_scales[so] = (uint8_t)(sx + 127);
+            }
           }
         }
       }
@@ -1116,7 +1160,7 @@ __global__ __launch_bounds__(256) void prep_transpose_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ dst_scales,
                                                              size_t dst_stride,
                                                              size_t dsts_stride, int row_stride,
-                                                             int row_off) {
+                                                             int row_off, int sc_cm, int n_rows) {
   __shared__ float tile[64][65];
   const int e = blockIdx.z;
   const int k0 = blockIdx.y * 64;
@@ -1147,8 +1191,10 @@ __global__ __launch_bounds__(256) void prep_transpose_kernel(const uint16_t* __r
       const float inv = mx_inv_scale(sx);
       uint8_t* d = dst + (size_t)e * dst_stride + (size_t)orow * K + k0 + half * 32;
       for (int q = 0; q < 32; ++q) d[q] = (uint8_t)e4m3_encode(tile[half * 32 + q][cc] * inv);
-      dst_scales[(size_t)e * dsts_stride + (size_t)orow * (K / kMxBlock) + (k0 >> 5) + half] =
-          (uint8_t)(sx + 127);
+      const int kb = (k0 >> 5) + half;  // MX block along K
+      const size_t so = sc_cm ? ((size_t)(kb >> 3) * n_rows + orow) * 8 + (kb & 7)
+                              : (size_t)orow * (K / kMxBlock) + kb;
+      dst_scales[(size_t)e * dsts_stride + so] = (uint8_t)(sx + 127);
     }
   }
 }
@@ -1178,7 +1224,7 @@ PreparedLayout prepared_layout(int E_loc, int h, int m, bool mx) {
 }
 
 struct FfnLayout {
-  size_t count, tiles, H, Hs, total;
+  size_t count, tiles, H, Hs, Rs, total;
   int max_tiles;
 };
 
@@ -1194,6 +1240,19 @@ int ffn_tile_rows(int R, int h, int m, int E_loc, bool mx) {
 }
 bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 
+// natural [R][K/32] scales -> chunk-major [K/256][R][8]; one thread per (row, chunk), rows fastest
+// so the writes are contiguous (K % 256 == 0)
+__global__ __launch_bounds__(256) void scales_chunk_major_kernel(const uint8_t* __restrict__ src,
+                                                                 int R, int K,
+                                                                 uint8_t* __restrict__ dst) {
+  const int nc = K / 256;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)R * nc) return;
+  const int r = (int)(i % R), cc = (int)(i / R);
+  const uint2 v = *reinterpret_cast<const uint2*>(src + (size_t)r * (K / kMxBlock) + 8 * cc);
+  *reinterpret_cast<uint2*>(dst + ((size_t)cc * R + r) * 8) = v;
+}
+
 FfnLayout ffn_layout(int R, int h, int m, int E_loc, bool mx) {
   FfnLayout L{};
   // room for 128-row tiles, the smallest any launch takes
@@ -1208,6 +1267,8 @@ FfnLayout ffn_layout(int R, int h, int m, int E_loc, bool mx) {
   if (mx) {
     L.Hs = off;
     off = align_up(off + (size_t)R * (m / kMxBlock));
+    L.Rs = off;  // the routed rows' scales, chunk-major (large-tile kernel)
+    off = align_up(off + (size_t)R * (h / kMxBlock));
   }
   L.total = off;
   return L;
@@ -1237,19 +1298,21 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
   const size_t s2 = (size_t)m * h;
   const size_t d2 = (size_t)h * m * el, d2s = (size_t)h * (m / kMxBlock);
   if (mx) {
+    // the large-tile kernel reads chunk-major weight scales, the small one natural ones
+    const int cm = ffn_big(h, m) ? 1 : 0;
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g1, dim3(256), 0, st, w_gate, h, m, s1,
-                       base + L.w1, base + L.w1s, d1, d1s, 64, 0);
+                       base + L.w1, base + L.w1s, d1, d1s, 64, 0, cm, 2 * m);
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g1, dim3(256), 0, st, w_up, h, m, s1,
-                       base + L.w1, base + L.w1s, d1, d1s, 64, 32);
+                       base + L.w1, base + L.w1s, d1, d1s, 64, 32, cm, 2 * m);
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g2, dim3(256), 0, st, w_down, m, h, s2,
-                       base + L.w2, base + L.w2s, d2, d2s, 32, 0);
+                       base + L.w2, base + L.w2s, d2, d2s, 32, 0, cm, h);
   } else {
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g1, dim3(256), 0, st, w_gate, h, m, s1,
-                       base + L.w1, nullptr, d1, 0, 64, 0);
+                       base + L.w1, nullptr, d1, 0, 64, 0, 0, 0);
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g1, dim3(256), 0, st, w_up, h, m, s1,
-                       base + L.w1, nullptr, d1, 0, 64, 32);
+                       base + L.w1, nullptr, d1, 0, 64, 32, 0, 0);
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g2, dim3(256), 0, st, w_down, m, h, s2,
-                       base + L.w2, nullptr, d2, 0, 32, 0);
+                       base + L.w2, nullptr, d2, 0, 32, 0, 0, 0);
   }
   return hipGetLastError();
 }
@@ -1322,6 +1385,16 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   if (big) {
     const dim3 g1 = big_grid(max_tiles, (2 * m) / kBigBN);
     const dim3 g2 = big_grid(max_tiles, h / kBigBN);
+    if (mx) {  // chunk-major scales throughout: weights (prepared so), rows, and H
+      const long long units = (long long)R * (h / 256);
+      hipLaunchKernelGGL(scales_chunk_major_kernel, dim3((unsigned)((units + 255) / 256)),
+                         dim3(256), 0, st, row_scales, R, h, w + F.Rs);
+      a1.row_scales = w + F.Rs;
+      a1.w_sc_cm = a1.r_sc_cm = a1.out_sc_cm = 1;
+      a1.sc_rows = R;
+      a2.w_sc_cm = a2.r_sc_cm = 1;
+      a2.sc_rows = R;
+    }
     if (mx && bm == 192) {  // never with save
       MOE_BIG(kEpiSwiglu, true, 192, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);

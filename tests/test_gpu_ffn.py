@@ -67,7 +67,8 @@ def test_expert_ffn_parity(case):
 
 
 def test_prepared_mx_weights_bit_exact():
-    """The MXFP8 prepared layout holds exactly the oracle's MX codes of each weight column."""
+    """The MXFP8 prepared layout holds exactly the oracle's MX codes and scales of each weight
+    column."""
     G = require_gpu()
     h, m, E_loc = 256, 256, 2
     wl = I.Workload(name="prep", T=1, h=h, m=m, E=E_loc, k=1, E_loc=E_loc, dtype="mxfp8",
@@ -81,7 +82,10 @@ def test_prepared_mx_weights_bit_exact():
     n1 = E_loc * 2 * m * h
     w1 = p[:n1].reshape(E_loc, 2 * m, h)
     off = (n1 + 255) // 256 * 256
-    w1s = p[off:off + E_loc * 2 * m * h // 32].reshape(E_loc, 2 * m, h // 32)
+    # scales chunk-major: [E][h/256][2m][8], the 8 block scales of one 256-element chunk of
+    # every weight row side by side
+    w1s = (p[off:off + E_loc * 2 * m * h // 32].reshape(E_loc, h // 256, 2 * m, 8)
+           .transpose(0, 2, 1, 3).reshape(E_loc, 2 * m, h // 32))
     for e in range(E_loc):
         qg, sg = F.mx_quantize(F.bf16_to_f64(wts[e][0]), axis=0)  # [h, m] along h
         rowsel = np.array([64 * (n // 32) + n % 32 for n in range(m)])
