@@ -228,7 +228,8 @@ moe_status moe_forward_views(const moe_shape* s, moe_dtype dt, void* ws,
  *
  * moe_prepare_bwd_weights: the backward's weight layout (offline), from the same bf16 weights as
  *   moe_prepare_weights: W_down rows [e][m][h] (K = h) and [W_gate | W_up] rows [e][h][2m]
- *   interleaved per 32 (K = 2m), MX-quantised along K for MOE_MXFP8.
+ *   interleaved per 32 (K = 2m), MX-quantised along K for MOE_MXFP8 (codes first, then the
+ *   scales chunk-major as in moe_prepare_weights: [e][K/256][rows][8]).
  * moe_backward: x [T][h] bf16 (the forward's input), dy [T][h] bf16, saved from moe_forward with
  *   the same shape and dtype, prepared_bwd from moe_prepare_bwd_weights. Outputs dx [T][h] bf16,
  *   dw_gate and dw_up [E_loc][h][m], dw_down [E_loc][m][h], float32 when dw_fp32 = 1, bf16 when 0

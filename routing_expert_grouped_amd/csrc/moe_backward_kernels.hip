@@ -17,6 +17,9 @@
 // expert's routed rows for the weight gradients. For the last, each expert's rows are padded with
 // zeros to a multiple of the GEMM's K step and stored transposed, [C][kpad_e], at offset
 // koff[e] * C, with E8M0 scales per 32 rows; blocks start at the expert's first row.
+// Every MX scale array the GEMMs read here is chunk-major: the 8 block scales of one 256-element
+// chunk of the reduction axis of each row side by side, [K/256][rows][8] (per expert for weights
+// and per expert segment for the transposed operands).
 #include "moe_internal.h"
 
 namespace moe {
@@ -33,12 +36,12 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
 //   W_down rows [e][m][h] stay as they are (K = h for dH = dO W_down^T);
 //   W_gate and W_up rows [e][h][m] are interleaved per 32 into [e][h][2m] (K = 2m for dA), gate
 //   blocks at 64 b, up blocks at 64 b + 32, the same order as the dG | dU columns.
-// One thread per block of 32.
+// One thread per block of 32. N: rows per expert (for the chunk-major scales).
 // ------------------------------------------------------------------------------------------------
 template <bool MX>
 __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* __restrict__ src,
                                                         long long nblocks, int Ks, int Kd,
-                                                        int bstride, int boff,
+                                                        int bstride, int boff, int N,
                                                         uint8_t* __restrict__ dst,
                                                         uint8_t* __restrict__ dst_s) {
   const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -65,7 +68,10 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* __restri
     uint4* d = reinterpret_cast<uint4*>(dst + kd);
     d[0] = make_uint4(c[0], c[1], c[2], c[3]);
     d[1] = make_uint4(c[4], c[5], c[6], c[7]);
-    dst_s[kd / kMxBlock] = (uint8_t)(sx + 127);
+    const long long e = row / N, n = row % N;
+    const int kb = (b * bstride + boff) / kMxBlock;  // block along the destination K
+    dst_s[e * N * (Kd / kMxBlock) + ((long long)(kb >> 3) * N + n) * 8 + (kb & 7)] =
+        (uint8_t)(sx + 127);
   } else {
     uint4* d = reinterpret_cast<uint4*>(dst + 2 * kd);
 #pragma unroll
@@ -117,7 +123,8 @@ __global__ __launch_bounds__(256) void uncombine_kernel(const uint16_t* __restri
                                                         const float* __restrict__ w,
                                                         const int32_t* __restrict__ offsets,
                                                         int E_loc, uint8_t* __restrict__ dO,
-                                                        uint8_t* __restrict__ dO_s, int h, int k) {
+                                                        uint8_t* __restrict__ dO_s, int R, int h,
+                                                        int k) {
   const int r = blockIdx.x;
   if (r >= offsets[E_loc]) return;
   const int a = perm[r];
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(256) void uncombine_kernel(const uint16_t* __restri
       uint4* d = reinterpret_cast<uint4*>(dO + (size_t)r * h + b * kMxBlock);
       d[0] = make_uint4(c[0], c[1], c[2], c[3]);
       d[1] = make_uint4(c[4], c[5], c[6], c[7]);
-      dO_s[(size_t)r * nb + b] = (uint8_t)(sx + 127);
+      dO_s[((size_t)(b >> 3) * R + r) * 8 + (b & 7)] = (uint8_t)(sx + 127);
     }
   } else {
     uint16_t* d = reinterpret_cast<uint16_t*>(dO) + (size_t)r * h;
@@ -257,7 +264,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     uint4* d = reinterpret_cast<uint4*>(dst + col_at + 32 * b);
     d[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     d[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-    dst_s[(col_at + 32 * b) / kMxBlock] = (uint8_t)(sx + 127);
+    const int kb = (q0 + 32 * b) / kMxBlock;  // block along the segment's K
+    dst_s[(size_t)kbase * C / kMxBlock + ((size_t)(kb >> 3) * C + c0 + c) * 8 + (kb & 7)] =
+        (uint8_t)(sx + 127);
   } else {
     const int b = tid >> 6;  // rows 16 b .. 16 b + 15
     uint32_t pw[8];
@@ -315,17 +324,17 @@ hipError_t launch_prepare_bwd_weights(const uint16_t* w_gate, const uint16_t* w_
   const dim3 g1((unsigned)((n1 + 255) / 256)), g2((unsigned)((n2 + 255) / 256));
   if (mx) {
     hipLaunchKernelGGL(prep_rows_kernel<true>, g1, dim3(256), 0, st, w_gate, n1, m, 2 * m, 64, 0,
-                       b + L.w1b, b + L.w1b_s);
+                       h, b + L.w1b, b + L.w1b_s);
     hipLaunchKernelGGL(prep_rows_kernel<true>, g1, dim3(256), 0, st, w_up, n1, m, 2 * m, 64, 32,
-                       b + L.w1b, b + L.w1b_s);
-    hipLaunchKernelGGL(prep_rows_kernel<true>, g2, dim3(256), 0, st, w_down, n2, h, h, 32, 0,
+                       h, b + L.w1b, b + L.w1b_s);
+    hipLaunchKernelGGL(prep_rows_kernel<true>, g2, dim3(256), 0, st, w_down, n2, h, h, 32, 0, m,
                        b + L.w2b, b + L.w2b_s);
   } else {
     hipLaunchKernelGGL(prep_rows_kernel<false>, g1, dim3(256), 0, st, w_gate, n1, m, 2 * m, 64, 0,
-                       b + L.w1b, nullptr);
+                       h, b + L.w1b, nullptr);
     hipLaunchKernelGGL(prep_rows_kernel<false>, g1, dim3(256), 0, st, w_up, n1, m, 2 * m, 64, 32,
-                       b + L.w1b, nullptr);
-    hipLaunchKernelGGL(prep_rows_kernel<false>, g2, dim3(256), 0, st, w_down, n2, h, h, 32, 0,
+                       h, b + L.w1b, nullptr);
+    hipLaunchKernelGGL(prep_rows_kernel<false>, g2, dim3(256), 0, st, w_down, n2, h, h, 32, 0, m,
                        b + L.w2b, nullptr);
   }
   return hipGetLastError();
@@ -343,10 +352,10 @@ hipError_t launch_uncombine(const uint16_t* dy, const int32_t* perm, const float
   uint8_t* d = reinterpret_cast<uint8_t*>(dO);
   if (mx)
     hipLaunchKernelGGL(uncombine_kernel<true>, dim3(R), dim3(256), 0, st, dy, perm, w, offsets,
-                       E_loc, d, dO_s, h, k);
+                       E_loc, d, dO_s, R, h, k);
   else
     hipLaunchKernelGGL(uncombine_kernel<false>, dim3(R), dim3(256), 0, st, dy, perm, w, offsets,
-                       E_loc, d, nullptr, h, k);
+                       E_loc, d, nullptr, R, h, k);
   return hipGetLastError();
 }
 

@@ -1041,7 +1041,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
                   (e4m3_encode(c4[2] * iu) << 16) | (e4m3_encode(c4[3] * iu) << 24);
             }
             // scale bytes of the dG block (lane group 0) and the dU block (lane group 1)
-            p.out_scales[(size_t)r * (N2 / kMxBlock) + (cg >> 5) + g] = (uint8_t)((g ? su_ : sg_) + 127);
+            const int kb = (cg >> 5) + g;  // MX block along 2m
+            const size_t so = p.out_sc_cm
+                                  ? ((size_t)(kb >> 3) * p.sc_rows + r) * 8 + (kb & 7)
+                                  : (size_t)r * (N2 / kMxBlock) + kb;
+            p.out_scales[so] = (uint8_t)((g ? su_ : sg_) + 127);
           }
         } else {
           if (r < row_end) {
@@ -1481,6 +1485,9 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
   a.out_scales = dgu_s;
   a.gu_in = gu;
   a.d_f32 = dgu_f32;
+  // MX: every scale array chunk-major (dO from the un-combine, the backward weights, dG | dU)
+  a.w_sc_cm = a.r_sc_cm = a.out_sc_cm = mx ? 1 : 0;
+  a.sc_rows = R;
 
   // dA = [dG | dU] [W_gate | W_up]^T (K = 2m, interleaved per 32 on both sides, N = h)
   GemmArgs b{};
@@ -1488,6 +1495,8 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
   b.row_scales = dgu_s;
   b.w = w1b;
   b.w_scales = w1b_s;
+  b.w_sc_cm = b.r_sc_cm = mx ? 1 : 0;
+  b.sc_rows = R;
   b.w_stride = (size_t)h * 2 * m * el;
   b.ws_stride = (size_t)h * (2 * m / kMxBlock);
   b.offsets = offsets;
@@ -1527,6 +1536,8 @@ hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_
   a.out_f32 = out_f32;
   a.out = dw_gate;
   a.out2 = dw_up;
+  a.w_sc_cm = a.r_sc_cm = mx ? 1 : 0;  // per expert segment, [kpad_e/256][C][8]
+  a.sc_rows = h;
   // dW_down [e] (m x h) = H_e^T dO_e: M side H^T (m rows), N side dO^T (h rows)
   GemmArgs b{};
   b.rows = Ht;
@@ -1540,6 +1551,8 @@ hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_
   b.split_gate_up = 0;
   b.out_f32 = out_f32;
   b.out = dw_down;
+  b.w_sc_cm = b.r_sc_cm = mx ? 1 : 0;
+  b.sc_rows = m;
   const dim3 ga = big_grid(a.tiles_total, a.N / kBigBN), gb = big_grid(b.tiles_total, b.N / kBigBN);
   if (mx) MOE_BIG(kEpiWgrad, true, 128, ga, a);
   else MOE_BIG(kEpiWgrad, false, 256, ga, a);
