@@ -126,6 +126,7 @@ moe_status check_router_shape(const moe_shape* s) {
 
 struct ForwardLayout {
   size_t logits, idx, w, counts, offsets, perm, inv, sched, rows, row_scales, ffn, out_rows;
+  size_t xf;  // the router's float32 copy of x: inside `rows` (free until the gather) if it fits
   size_t shared_off, shared_ffn, shared_out, total;
   bool router;
 };
@@ -153,6 +154,10 @@ ForwardLayout forward_layout(const moe_shape* s, moe_dtype dt, bool router) {
   L.row_scales = mx ? take(R * (s->h / kMxBlock)) : 0;
   L.ffn = take(ffn_workspace_bytes((int)R, s->h, s->m, s->E_loc, mx));
   L.out_rows = take(R * s->h * 2);
+  if (router) {
+    const size_t need = router_xf_bytes(s->T, s->h);
+    L.xf = need <= R * s->h * (mx ? 1 : 2) ? L.rows : take(need);
+  }
   if (s->m_shared > 0) {
     L.shared_off = take(2 * 4);
     L.shared_ffn = take(ffn_workspace_bytes(s->T, s->h, s->m_shared, 1, false));
@@ -344,7 +349,8 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
     float* logits = reinterpret_cast<float*>(b + L.logits);
     int32_t* idx = reinterpret_cast<int32_t*>(b + L.idx);
     float* w = reinterpret_cast<float*>(b + L.w);
-    e = launch_router_logits(x, w_router, bias, logits, T, h, s->E, hs);
+    e = launch_router_logits_xf(x, w_router, bias, logits, T, h, s->E,
+                                reinterpret_cast<float*>(b + L.xf), hs);
     mark(1);
     if (e == hipSuccess) e = launch_topk_softmax(logits, idx, w, T, s->E, k, hs);
     a_idx = idx;

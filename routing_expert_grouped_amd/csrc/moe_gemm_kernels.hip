@@ -1233,14 +1233,18 @@ struct FfnLayout {
 };
 
 // rows per M tile: the large-tile kernel (h % 256 == 0, m % 128 == 0) takes 256 rows (BF16) when
-// the experts hold 224 rows or more on average, 192 rows (MXFP8) from 128 rows on average, else
-// 128; the small-tile kernel always 128
+// the experts hold 224 rows or more on average and there are enough tiles, 192 rows (MXFP8) from
+// 128 rows on average, else 128; the small-tile kernel always 128
 int ffn_tile_rows(int R, int h, int m, int E_loc, bool mx) {
   if (h % kBigBN || (2 * m) % kBigBN) return kBM;
   // MXFP8: a 256-row tile does not fit the register file; 192 rows (three 32-row fragments per
   // wave) does, and wastes less on experts of a few hundred rows than two 128-row tiles
   if (mx) return (R / E_loc >= 128) ? 192 : 128;
-  return (R / E_loc >= 224) ? 256 : 128;
+  // BF16: 256 rows when the experts are large enough and the 256-row tiles still give every CU
+  // a tile (a launch of fewer tiles than CUs, e.g. the shared expert over 2048 tokens, runs
+  // faster as twice as many 128-row tiles)
+  const long long tiles256 = (long long)((R + 255) / 256) * ((2 * m) / kBigBN);
+  return (R / E_loc >= 224 && tiles256 >= 256) ? 256 : 128;
 }
 bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 

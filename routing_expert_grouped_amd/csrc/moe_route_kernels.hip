@@ -59,6 +59,60 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
   }
 }
 
+// x as float32, 8 tokens interleaved: xf[g][i][j] = x[8g + j][i] (zeros past T), [ceil(T/8)][h][8].
+// One thread per (group g, column i); the 8 values it writes are 32 contiguous bytes.
+__global__ __launch_bounds__(256) void x_interleave_kernel(const uint16_t* __restrict__ x, int T,
+                                                           int h, float* __restrict__ xf) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int g = blockIdx.y;
+  if (i >= h) return;
+  float v[kRouterTokens];
+#pragma unroll
+  for (int j = 0; j < kRouterTokens; ++j) {
+    const int t = g * kRouterTokens + j;
+    v[j] = t < T ? bf16_to_f32(x[(size_t)t * h + i]) : 0.0f;
+  }
+  f32x4_t* d = reinterpret_cast<f32x4_t*>(xf + ((size_t)g * h + i) * kRouterTokens);
+  d[0] = (f32x4_t){v[0], v[1], v[2], v[3]};
+  d[1] = (f32x4_t){v[4], v[5], v[6], v[7]};
+}
+
+// The same logits, in the same order, from the interleaved float32 x: the 64 scalar operands of
+// a step of 8 columns are 256 contiguous bytes (scalar loads, no conversion on the scalar unit,
+// which otherwise issues as many instructions as the FMAs).
+__global__ __launch_bounds__(kRouterThreads) void router_logits_xf_kernel(
+    const float* __restrict__ xf, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int h, int E) {
+  const int e = blockIdx.y * kRouterThreads + threadIdx.x;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
+  const uint4* wrow = reinterpret_cast<const uint4*>(w + (size_t)e_ld * h);
+  const float* xg = xf + (size_t)blockIdx.x * h * kRouterTokens;
+  float acc[kRouterTokens];
+#pragma unroll
+  for (int tt = 0; tt < kRouterTokens; ++tt) acc[tt] = 0.0f;
+
+  const int nvec = h / 8;
+  for (int v = 0; v < nvec; ++v) {
+    const uint4 wv = wrow[v];
+    const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                         bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+    const float* xs = xg + (size_t)v * 8 * kRouterTokens;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int tt = 0; tt < kRouterTokens; ++tt)
+        acc[tt] = __builtin_fmaf(xs[q * kRouterTokens + tt], wf[q], acc[tt]);
+  }
+  if (e < E) {
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < kRouterTokens; ++tt) {
+      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = bias ? acc[tt] + b : acc[tt];
+    }
+  }
+}
+
 // "a ranks before b": larger logit first, then the lower expert index.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -136,6 +190,21 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, con
   dim3 grid((T + kRouterTokens - 1) / kRouterTokens, (E + kRouterThreads - 1) / kRouterThreads);
   hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRouterThreads), 0, st, x, w_router, bias,
                      logits, T, h, E);
+  return hipGetLastError();
+}
+
+size_t router_xf_bytes(int T, int h) {
+  return (size_t)((T + kRouterTokens - 1) / kRouterTokens) * kRouterTokens * h * sizeof(float);
+}
+
+hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                   float* logits, int T, int h, int E, float* xf, hipStream_t st) {
+  const int groups = (T + kRouterTokens - 1) / kRouterTokens;
+  hipLaunchKernelGGL(x_interleave_kernel, dim3((h + 255) / 256, groups), dim3(256), 0, st, x, T, h,
+                     xf);
+  dim3 grid(groups, (E + kRouterThreads - 1) / kRouterThreads);
+  hipLaunchKernelGGL(router_logits_xf_kernel, grid, dim3(kRouterThreads), 0, st, xf, w_router,
+                     bias, logits, T, h, E);
   return hipGetLastError();
 }
 
