@@ -13,16 +13,19 @@ from tests._gpu_helpers import (BF16_TOL, MX_TOL, dev, dev_bf16, host_f64_from_b
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # dtype, rows per expert, h, m
+    # dtype, rows per expert, h, m (tile heights: BF16 256 rows from 224 rows per expert when the
+    # 256-row tiles number 256 or more; MXFP8 192 rows from 128 rows per expert; else 128;
+    # h % 256 != 0 takes the small-tile kernel)
     ("bf16", [16, 0, 40, 200], 256, 128),
-    ("bf16", [1, 129, 0, 300, 127, 2], 384, 192),
+    ("bf16", [1, 129, 0, 300, 127, 2], 384, 192),  # small-tile kernel
     ("bf16", [517], 512, 256),
-    ("bf16", [300, 0, 700, 31], 256, 256),     # 256-row tiles, several experts
-    ("bf16", [2000, 513], 1024, 512),          # many K stages, several N tiles
+    ("bf16", [300, 0, 700, 31], 256, 256),         # 128-row tiles (too few 256-row ones)
+    ("bf16", [2000, 513], 1024, 512),              # many K stages, several N tiles
+    ("bf16", [1100, 0, 900, 61], 256, 4096),       # 256-row tiles (288 of them)
     ("mxfp8", [16, 0, 40, 200], 256, 256),
     ("mxfp8", [1, 129, 0, 300, 127, 2], 512, 256),
     ("mxfp8", [0, 0, 259], 768, 512),
-    ("mxfp8", [600, 0, 301], 512, 256),        # 256-row tiles
+    ("mxfp8", [600, 0, 301], 512, 256),            # 192-row tiles
     ("mxfp8", [1500, 700], 1024, 512),
 ]
 
