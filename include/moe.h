@@ -76,8 +76,12 @@ int moe_abi_version(void);
  *   MOE_BF16 : W1[e][2m][h] bf16 (row n = output column n of GEMM-1; gate and up columns
  *              interleaved in blocks of 32: rows 64c..64c+31 are gate columns 32c..32c+31,
  *              rows 64c+32..64c+63 the up columns of the same range), then W2[e][h][m] bf16
- *              (W_down transposed).
- *   MOE_MXFP8: the same two matrices as E4M3 codes, each followed by its E8M0 scales; blocks
+ *              (W_down transposed). When h % 256 == 0 and 2m % 256 == 0 (the large-tile
+ *              kernels) each matrix is stored K-tiled: [e][rows/256][K bytes/128][256][128
+ *              bytes], i.e. every 128-byte K slice of a 256-row panel is one contiguous 32 KB
+ *              block (one pipeline stage of the GEMM, read with whole DRAM pages).
+ *   MOE_MXFP8: the same two matrices as E4M3 codes (K-tiled as above; always so, since MXFP8
+ *              needs h % 256 == 0 and m % 256 == 0), each followed by its E8M0 scales; blocks
  *              of 32 run along h for W1 and along m for W2, i.e. along each GEMM's reduction
  *              axis, and the scales are stored chunk-major: [e][h/256][2m][8] and
  *              [e][m/256][h][8], the 8 block scales of one 256-element chunk of a row side by

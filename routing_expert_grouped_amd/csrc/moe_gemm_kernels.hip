@@ -75,6 +75,9 @@ struct GemmArgs {
   int r_sc_cm;
   int out_sc_cm;
   int sc_rows;
+  // large-tile kernel: weight codes K-tiled, [E][N/256][K bytes/128][256][128 bytes] (each stage
+  // of a 256-row weight panel is one contiguous 32 KB block), else natural [E][N][K]
+  int w_tiled;
 };
 
 // Epilogue (and grouping) modes of the large-tile kernel.
@@ -575,7 +578,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     const int c = (id % SLOTS) ^ big_swz<RB>(row);
     const uint32_t cb = 16 * c;
     if (q < QW) {
-      src[q] = (uint32_t)((n0 + row) * ldk) + cb;
+      src[q] = p.w_tiled ? (uint32_t)((size_t)(n0 / BN) * ldk * BN) + row * RB + cb
+                         : (uint32_t)((n0 + row) * ldk) + cb;
     } else {
       int r = row0 + row - BN;
       r = r < row_end ? r : row_end - 1;  // rows past the expert's end are never stored
@@ -584,6 +588,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   }
   // stage j holds K bytes [RB j, RB j + RB) of every row (whole cache lines for RB = 128)
   auto stage_off = [&](int j) -> size_t { return (size_t)RB * j; };
+  const uint32_t wstage_bytes = p.w_tiled ? (uint32_t)WSTAGE : (uint32_t)RB;  // per weight stage
   const int nk = (int)(ldk / RB);
   const int nchunks = MX ? nk / PC : 0;
   // first unit of part t (t = SPS: the end)
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   auto issue_part = [&](int b, int part) {
     const int sw = b + NS - 1, sr = b + NSR - 1;
     const bool hw = sw >= 0 && sw < nk, hr = sr >= 0 && sr < nk;
-    const uint32_t offw = (uint32_t)stage_off(sw), offr = (uint32_t)stage_off(sr);
+    const uint32_t offw = wstage_bytes * (uint32_t)(sw < 0 ? 0 : sw), offr = (uint32_t)stage_off(sr);
     uint8_t* bw = wbuf(sw < 0 ? 0 : sw) + wave * 1024;
     uint8_t* br = rbuf(sr < 0 ? 0 : sr) + wave * 1024;
     const int q0 = part_start(part), q1 = part_start(part + 1);
@@ -802,7 +807,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     const uint8_t* rbw = LAST ? wbuf(j + 1) : wbuf(j);
     const uint8_t* rbr = LAST ? rbuf(j + 1) : rbuf(j);
     const int rt = LAST ? 0 : t + 1;
-    const uint32_t doffw = (uint32_t)stage_off(j + NS - 1);  // point j's groups
+    const uint32_t doffw = wstage_bytes * (uint32_t)(j + NS - 1);  // point j's groups
     const uint32_t doffr = (uint32_t)stage_off(j + NSR - 1);
     uint8_t* dbw = wbuf(j + NS - 1) + wave * 1024;  // stage j-1's ring slots
     uint8_t* dbr = rbuf(j + NSR - 1) + wave * 1024;
@@ -1164,7 +1169,8 @@ __global__ __launch_bounds__(256) void prep_transpose_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ dst_scales,
                                                              size_t dst_stride,
                                                              size_t dsts_stride, int row_stride,
-                                                             int row_off, int sc_cm, int n_rows) {
+                                                             int row_off, int sc_cm, int n_rows,
+                                                             int tiled) {
   __shared__ float tile[64][65];
   const int e = blockIdx.z;
   const int k0 = blockIdx.y * 64;
@@ -1176,13 +1182,21 @@ __global__ __launch_bounds__(256) void prep_transpose_kernel(const uint16_t* __r
     tile[kk][cc] = bf16_to_f32(s[(size_t)(k0 + kk) * Ns + c0 + cc]);
   }
   __syncthreads();
+  // byte address of byte kb of destination row orow: natural orow * K bytes + kb, or K-tiled
+  // (256-row panels, 128-byte stages; n_rows % 256 == 0 and the row's bytes % 128 == 0)
+  const size_t rowb = (size_t)K * (MX ? 1 : 2);
+  auto at = [&](int orow, size_t kb) -> size_t {
+    if (!tiled) return (size_t)orow * rowb + kb;
+    return (((size_t)(orow >> 8) * (rowb >> 7) + (kb >> 7)) * 256 + (orow & 255)) * 128 + (kb & 127);
+  };
   if constexpr (!MX) {
-    uint16_t* d = reinterpret_cast<uint16_t*>(dst + (size_t)e * dst_stride);
+    uint8_t* d = dst + (size_t)e * dst_stride;
     for (int i = tid; i < 64 * 64; i += 256) {
       const int cc = i >> 6, kk = i & 63;
       const int n = c0 + cc;
       const int orow = (n >> 5) * row_stride + row_off + (n & 31);
-      d[(size_t)orow * K + k0 + kk] = (uint16_t)f32_to_bf16_bits(tile[kk][cc]);
+      *reinterpret_cast<uint16_t*>(d + at(orow, (size_t)2 * (k0 + kk))) =
+          (uint16_t)f32_to_bf16_bits(tile[kk][cc]);
     }
   } else {
     if (tid < 128) {
@@ -1193,7 +1207,7 @@ __global__ __launch_bounds__(256) void prep_transpose_kernel(const uint16_t* __r
       for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(tile[half * 32 + q][cc]));
       const int sx = mx_block_exponent(amax);
       const float inv = mx_inv_scale(sx);
-      uint8_t* d = dst + (size_t)e * dst_stride + (size_t)orow * K + k0 + half * 32;
+      uint8_t* d = dst + (size_t)e * dst_stride + at(orow, (size_t)k0 + half * 32);
       for (int q = 0; q < 32; ++q) d[q] = (uint8_t)e4m3_encode(tile[half * 32 + q][cc] * inv);
       const int kb = (k0 >> 5) + half;  // MX block along K
       const size_t so = sc_cm ? ((size_t)(kb >> 3) * n_rows + orow) * 8 + (kb & 7)
@@ -1305,22 +1319,22 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
   dim3 g2(h / 64, m / 64, E_loc);
   const size_t s2 = (size_t)m * h;
   const size_t d2 = (size_t)h * m * el, d2s = (size_t)h * (m / kMxBlock);
+  // the large-tile kernel reads K-tiled codes and chunk-major scales, the small one natural ones
+  const int big = ffn_big(h, m) ? 1 : 0;
   if (mx) {
-    // the large-tile kernel reads chunk-major weight scales, the small one natural ones
-    const int cm = ffn_big(h, m) ? 1 : 0;
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g1, dim3(256), 0, st, w_gate, h, m, s1,
-                       base + L.w1, base + L.w1s, d1, d1s, 64, 0, cm, 2 * m);
+                       base + L.w1, base + L.w1s, d1, d1s, 64, 0, big, 2 * m, big);
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g1, dim3(256), 0, st, w_up, h, m, s1,
-                       base + L.w1, base + L.w1s, d1, d1s, 64, 32, cm, 2 * m);
+                       base + L.w1, base + L.w1s, d1, d1s, 64, 32, big, 2 * m, big);
     hipLaunchKernelGGL(prep_transpose_kernel<true>, g2, dim3(256), 0, st, w_down, m, h, s2,
-                       base + L.w2, base + L.w2s, d2, d2s, 32, 0, cm, h);
+                       base + L.w2, base + L.w2s, d2, d2s, 32, 0, big, h, big);
   } else {
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g1, dim3(256), 0, st, w_gate, h, m, s1,
-                       base + L.w1, nullptr, d1, 0, 64, 0, 0, 0);
+                       base + L.w1, nullptr, d1, 0, 64, 0, 0, 0, big);
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g1, dim3(256), 0, st, w_up, h, m, s1,
-                       base + L.w1, nullptr, d1, 0, 64, 32, 0, 0);
+                       base + L.w1, nullptr, d1, 0, 64, 32, 0, 0, big);
     hipLaunchKernelGGL(prep_transpose_kernel<false>, g2, dim3(256), 0, st, w_down, m, h, s2,
-                       base + L.w2, nullptr, d2, 0, 32, 0, 0, 0);
+                       base + L.w2, nullptr, d2, 0, 32, 0, 0, 0, big);
   }
   return hipGetLastError();
 }
@@ -1393,6 +1407,7 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   if (big) {
     const dim3 g1 = big_grid(max_tiles, (2 * m) / kBigBN);
     const dim3 g2 = big_grid(max_tiles, h / kBigBN);
+    a1.w_tiled = a2.w_tiled = 1;  // prepared K-tiled
     if (mx) {  // chunk-major scales throughout: weights (prepared so), rows, and H
       const long long units = (long long)R * (h / 256);
       hipLaunchKernelGGL(scales_chunk_major_kernel, dim3((unsigned)((units + 255) / 256)),

@@ -70,8 +70,8 @@ def test_expert_ffn_parity(case):
 
 
 def test_prepared_mx_weights_bit_exact():
-    """The MXFP8 prepared layout holds exactly the oracle's MX codes and scales of each weight
-    column."""
+    """The MXFP8 prepared layout (K-tiled codes, chunk-major scales) holds exactly the oracle's MX
+    codes and scales of each weight column."""
     G = require_gpu()
     h, m, E_loc = 256, 256, 2
     wl = I.Workload(name="prep", T=1, h=h, m=m, E=E_loc, k=1, E_loc=E_loc, dtype="mxfp8",
@@ -83,7 +83,10 @@ def test_prepared_mx_weights_bit_exact():
     torch.cuda.synchronize()
     p = prepared.cpu().numpy()
     n1 = E_loc * 2 * m * h
-    w1 = p[:n1].reshape(E_loc, 2 * m, h)
+    # codes K-tiled: [E][2m/256][h/128][256][128], one contiguous 32 KB block per 128-byte stage of
+    # a 256-row panel
+    w1 = (p[:n1].reshape(E_loc, 2 * m // 256, h // 128, 256, 128).transpose(0, 1, 3, 2, 4)
+          .reshape(E_loc, 2 * m, h))
     off = (n1 + 255) // 256 * 256
     # scales chunk-major: [E][h/256][2m][8], the 8 block scales of one 256-element chunk of
     # every weight row side by side
