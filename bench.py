@@ -77,12 +77,18 @@ def layer_flops(wl) -> dict:
 
 
 def stage_bytes(wl) -> dict:
-    """Algorithmic HBM bytes of the bandwidth-bound stages (each byte moved once)."""
+    """Algorithmic HBM bytes of the bandwidth-bound stages (each byte moved once).
+
+    On the large-tile shapes (h % 256 == 0, 2m % 256 == 0: every benchmark workload) moe_forward
+    gathers the routed rows inside GEMM-1's loads: the gather stage is then only the MXFP8
+    per-token quantisation (read x, write T rows of codes and scales), or nothing for BF16."""
     R, T, h, k = wl.T * wl.k, wl.T, wl.h, wl.k
     mx = wl.dtype == "mxfp8"
     row_b = h * (1 + 1 / 32) if mx else 2 * h
+    fused = h % 256 == 0 and (2 * wl.m) % 256 == 0
+    gather = (T * h * 2 + T * row_b if mx else 0) if fused else T * h * 2 + R * row_b + R * 4
     return {
-        "gather": T * h * 2 + R * row_b + R * 4,                       # read x once, write R rows
+        "gather": gather,
         "combine": R * h * 2 + R * 8 + T * h * 2 + (T * h * 2 if wl.m_shared else 0),
         "topk": T * wl.E * 4 + R * 8 if wl.mode == "router" else 0,
     }

@@ -175,6 +175,10 @@ moe_status moe_combine(const moe_shape* s, const uint16_t* out_rows, const int32
  *   float32. Needs h % 256 == 0 and m % 256 == 0 (else MOE_EUNSUPPORTED).
  * ws: moe_forward_workspace_bytes() bytes. The intermediates stay in it; moe_forward_views()
  *   gives their addresses.
+ * Gather: when h % 256 == 0 and 2m % 256 == 0 the first grouped GEMM reads routed row r straight
+ *   from token perm[r] / k (of x, or of x quantised once per token for MXFP8) with its own loads,
+ *   so the forward writes no routed-row copy; the result is the one moe_permute + moe_expert_ffn
+ *   give (the same values enter the same MFMAs).
  * ------------------------------------------------------------------------------------------- */
 size_t moe_forward_workspace_bytes(const moe_shape* s, moe_dtype dt);
 size_t moe_saved_bytes(const moe_shape* s, moe_dtype dt);
@@ -207,8 +211,12 @@ typedef struct {
   int32_t* offsets;    /* [E_loc+1] */
   int32_t* perm;       /* [R] */
   int32_t* inv;        /* [R] */
-  void* rows;          /* [R][h] bf16 or E4M3 */
-  uint8_t* row_scales; /* [R][h/32]   MXFP8 only */
+  void* rows;          /* [R][h] bf16 or E4M3: the routed rows, when the forward materialises
+                          them (h % 256 != 0 or 2m % 256 != 0); on the large-tile shapes GEMM-1
+                          gathers them itself and this buffer holds, for MXFP8, the tokens
+                          quantised once ([T][h] codes), for BF16 scratch */
+  uint8_t* row_scales; /* [R][h/32], MXFP8 only (large-tile shapes: the tokens' scales,
+                          [h/256][T][8]) */
   uint16_t* out_rows;  /* [R][h] bf16 */
   uint16_t* shared_out;/* [T][h] bf16 shared expert output, if any */
 } moe_forward_views_t;

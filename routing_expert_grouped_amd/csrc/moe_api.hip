@@ -366,20 +366,36 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
   if (e == hipSuccess)
     e = launch_schedule(a_idx, R, s->E_loc, counts, offsets, perm, inv, b + L.sched, hs);
   mark(3);
+  // On the large-tile GEMMs the gather is done by GEMM-1's own loads (routed row r reads token
+  // perm[r] / k): BF16 reads x itself; MXFP8 quantises each token once into the row buffer
+  // (codes [T][h], chunk-major scales) and GEMM-1 reads those. Otherwise the routed rows are
+  // materialised by the gather kernels, as moe_permute does.
+  const bool fused_gather = ffn_big(h, s->m);
   if (e == hipSuccess) {
-    if (mx)
+    if (fused_gather) {
+      if (mx) e = launch_quantize_tokens_mxfp8(x, b + L.rows, b + L.row_scales, T, h, hs);
+    } else if (mx) {
       e = launch_gather_mxfp8(x, inv, b + L.rows, b + L.row_scales, T, h, k, hs);
-    else
+    } else {
       e = launch_gather_bf16(x, inv, reinterpret_cast<uint16_t*>(b + L.rows), T, h, k, hs);
+    }
   }
   mark(4);
   uint16_t* out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
   uint8_t* sv = reinterpret_cast<uint8_t*>(saved);
   const SavedLayout SL = saved_layout(s);
-  if (e == hipSuccess)
-    e = launch_expert_ffn(b + L.rows, mx ? b + L.row_scales : nullptr, offsets, prepared, out_rows,
-                          b + L.ffn, R, h, s->m, s->E_loc, mx, hs, ev ? ev + 5 : nullptr,
-                          sv ? reinterpret_cast<float*>(sv + SL.gu) : nullptr);
+  float* gu_save = sv ? reinterpret_cast<float*>(sv + SL.gu) : nullptr;
+  if (e == hipSuccess) {
+    if (fused_gather)
+      e = launch_expert_ffn(mx ? static_cast<const void*>(b + L.rows) : x,
+                            mx ? b + L.row_scales : nullptr, offsets, prepared, out_rows, b + L.ffn,
+                            R, h, s->m, s->E_loc, mx, hs, ev ? ev + 5 : nullptr, gu_save, perm, k,
+                            T, /*scales_cm=*/true);
+    else
+      e = launch_expert_ffn(b + L.rows, mx ? b + L.row_scales : nullptr, offsets, prepared,
+                            out_rows, b + L.ffn, R, h, s->m, s->E_loc, mx, hs,
+                            ev ? ev + 5 : nullptr, gu_save);
+  }
   uint16_t* shared_out = nullptr;
   if (e == hipSuccess && s->m_shared > 0) {
     int32_t* soff = reinterpret_cast<int32_t*>(b + L.shared_off);

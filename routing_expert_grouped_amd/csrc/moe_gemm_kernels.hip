@@ -74,7 +74,12 @@ struct GemmArgs {
   int w_sc_cm;
   int r_sc_cm;
   int out_sc_cm;
-  int sc_rows;
+  int sc_rows;      // rows of the chunk-major routed-row (input) scale array
+  int out_sc_rows;  // rows of the chunk-major output scale array
+  // large-tile kernel, routed-row operand gathered on the fly: routed row r reads row
+  // row_src[r] / row_div of `rows` (and of its scales), e.g. token perm[r] / k of x; null: row r
+  const int32_t* row_src;
+  int row_div;
   // large-tile kernel: weight codes K-tiled, [E][N/256][K bytes/128][256][128 bytes] (each stage
   // of a 256-row weight panel is one contiguous 32 KB block), else natural [E][N][K]
   int w_tiled;
@@ -583,6 +588,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     } else {
       int r = row0 + row - BN;
       r = r < row_end ? r : row_end - 1;  // rows past the expert's end are never stored
+      if (p.row_src) r = p.row_src[r] / p.row_div;
       src[q] = (uint32_t)(r * ldk) + cb;
     }
   }
@@ -636,6 +642,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     for (int j = 0; j < NJ; ++j) {
       int r = row0 + (BM / 2) * wm + 32 * j + li;
       r = r < row_end ? r : row_end - 1;
+      if (p.row_src) r = p.row_src[r] / p.row_div;
       sr_off[j] = (uint32_t)r * r_rs;
     }
   }
@@ -969,7 +976,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
             if (g == 0) {
               const int kb = col0 >> 5;  // MX block along m
               const size_t so = p.out_sc_cm
-                                    ? ((size_t)(kb >> 3) * p.sc_rows + r) * 8 + (kb & 7)
+                                    ? ((size_t)(kb >> 3) * p.out_sc_rows + r) * 8 + (kb & 7)
                                     : (size_t)r * (Hn / kMxBlock) + kb;
               p.out_scales[so] = (uint8_t)(sx + 127);
             }
@@ -1048,7 +1055,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
             // scale bytes of the dG block (lane group 0) and the dU block (lane group 1)
             const int kb = (cg >> 5) + g;  // MX block along 2m
             const size_t so = p.out_sc_cm
-                                  ? ((size_t)(kb >> 3) * p.sc_rows + r) * 8 + (kb & 7)
+                                  ? ((size_t)(kb >> 3) * p.out_sc_rows + r) * 8 + (kb & 7)
                                   : (size_t)r * (N2 / kMxBlock) + kb;
             p.out_scales[so] = (uint8_t)((g ? su_ : sg_) + 127);
           }
@@ -1260,7 +1267,6 @@ int ffn_tile_rows(int R, int h, int m, int E_loc, bool mx) {
   const long long tiles256 = (long long)((R + 255) / 256) * ((2 * m) / kBigBN);
   return (R / E_loc >= 224 && tiles256 >= 256) ? 256 : 128;
 }
-bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 
 // natural [R][K/32] scales -> chunk-major [K/256][R][8]; one thread per (row, chunk), rows fastest
 // so the writes are contiguous (K % 256 == 0)
@@ -1297,6 +1303,8 @@ FfnLayout ffn_layout(int R, int h, int m, int E_loc, bool mx) {
 }
 
 }  // namespace
+
+bool ffn_big(int h, int m) { return h % kBigBN == 0 && (2 * m) % kBigBN == 0; }
 
 size_t prepared_bytes(int E_loc, int h, int m, bool mx) {
   return prepared_layout(E_loc, h, m, mx).total;
@@ -1355,7 +1363,8 @@ static dim3 big_grid(int max_mt, int nt) {
 hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
                              const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
                              int m, int E_loc, bool mx, hipStream_t st, const hipEvent_t* ev,
-                             float* gu_out) {
+                             float* gu_out, const int32_t* row_src, int row_div, int src_rows,
+                             bool scales_cm) {
   const bool save = gu_out != nullptr;
   // a forward that keeps G and U takes 128-row tiles (the 256-row BF16 variant with the extra
   // stores does not fit the register file)
@@ -1408,13 +1417,19 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
     const dim3 g1 = big_grid(max_tiles, (2 * m) / kBigBN);
     const dim3 g2 = big_grid(max_tiles, h / kBigBN);
     a1.w_tiled = a2.w_tiled = 1;  // prepared K-tiled
+    a1.row_src = row_src;  // GEMM-1 may read its rows through an index (GEMM-2 reads H)
+    a1.row_div = row_div;
+    const int n_src = row_src ? src_rows : R;  // rows of `rows` and of its scales
     if (mx) {  // chunk-major scales throughout: weights (prepared so), rows, and H
-      const long long units = (long long)R * (h / 256);
-      hipLaunchKernelGGL(scales_chunk_major_kernel, dim3((unsigned)((units + 255) / 256)),
-                         dim3(256), 0, st, row_scales, R, h, w + F.Rs);
-      a1.row_scales = w + F.Rs;
+      if (!scales_cm) {
+        const long long units = (long long)n_src * (h / 256);
+        hipLaunchKernelGGL(scales_chunk_major_kernel, dim3((unsigned)((units + 255) / 256)),
+                           dim3(256), 0, st, row_scales, n_src, h, w + F.Rs);
+        a1.row_scales = w + F.Rs;
+      }
       a1.w_sc_cm = a1.r_sc_cm = a1.out_sc_cm = 1;
-      a1.sc_rows = R;
+      a1.sc_rows = n_src;
+      a1.out_sc_rows = R;
       a2.w_sc_cm = a2.r_sc_cm = 1;
       a2.sc_rows = R;
     }
@@ -1440,7 +1455,8 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
     if (ev) (void)hipEventRecord(ev[2], st);
     return hipGetLastError();
   }
-  if (gu_out) return hipErrorInvalidValue;  // G and U are only kept by the large-tile kernel
+  // G and U are only kept, rows only gathered through an index, by the large-tile kernel
+  if (gu_out || row_src) return hipErrorInvalidValue;
   dim3 grid1(max_tiles, (2 * m) / kBN);
   dim3 grid2(max_tiles, h / kBN);
   if (mx)
@@ -1506,7 +1522,7 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
   a.d_f32 = dgu_f32;
   // MX: every scale array chunk-major (dO from the un-combine, the backward weights, dG | dU)
   a.w_sc_cm = a.r_sc_cm = a.out_sc_cm = mx ? 1 : 0;
-  a.sc_rows = R;
+  a.sc_rows = a.out_sc_rows = R;
 
   // dA = [dG | dU] [W_gate | W_up]^T (K = 2m, interleaved per 32 on both sides, N = h)
   GemmArgs b{};

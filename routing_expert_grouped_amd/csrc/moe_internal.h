@@ -112,6 +112,10 @@ hipError_t launch_gather_bf16(const uint16_t* x, const int32_t* inv, uint16_t* r
                               int k, hipStream_t st);
 hipError_t launch_gather_mxfp8(const uint16_t* x, const int32_t* inv, uint8_t* rows,
                                uint8_t* scales, int T, int h, int k, hipStream_t st);
+// x quantised once per token: codes [T][h] E4M3, scales chunk-major [h/256][T][8] E8M0 (h % 256
+// == 0), for a grouped GEMM that gathers the routed rows through perm itself
+hipError_t launch_quantize_tokens_mxfp8(const uint16_t* x, uint8_t* codes, uint8_t* scales_cm,
+                                        int T, int h, hipStream_t st);
 
 // Grouped GEMMs + weight preparation (moe_gemm_kernels.hip)
 size_t ffn_workspace_bytes(int R, int h, int m, int E_loc, bool mx);
@@ -122,10 +126,17 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
 // ev (optional): three events recorded after the tile table, GEMM-1 and GEMM-2.
 // gu_out (optional, large-tile shapes only): GEMM-1's G and U as float32 [R][2m], gate/up
 // interleaved per 32 like the prepared W1 rows, kept for a backward pass.
+// row_src (optional, large-tile shapes only): GEMM-1 reads routed row r from row
+// row_src[r] / row_div of `rows` ([src_rows][h], e.g. the tokens x with row_src = perm,
+// row_div = k: the gather done by the GEMM's own loads). scales_cm: row_scales are already
+// chunk-major [h/256][rows][8] (else natural [rows][h/32]).
 hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const int32_t* offsets,
                              const void* prepared, uint16_t* out_rows, void* ws, int R, int h,
                              int m, int E_loc, bool mx, hipStream_t st,
-                             const hipEvent_t* ev = nullptr, float* gu_out = nullptr);
+                             const hipEvent_t* ev = nullptr, float* gu_out = nullptr,
+                             const int32_t* row_src = nullptr, int row_div = 1, int src_rows = 0,
+                             bool scales_cm = false);
+bool ffn_big(int h, int m);
 
 // Backward GEMMs (moe_gemm_kernels.hip). Both need h % 256 == 0 and m % 256 == 0.
 // K segments of the weight gradients: each expert's routed rows padded to a multiple of this

@@ -148,15 +148,18 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
 
 // MXFP8 gather, one workgroup per token: each thread quantises one block of 32 values of x[t]
 // once (amax, E8M0 exponent, E4M3 codes) and writes the codes and the scale to the k rows.
+// inv == nullptr: one copy, to row t (the tokens quantised in place of the routed rows, for a
+// GEMM that gathers them itself). sc_cm_rows > 0: scales chunk-major [h/256][sc_cm_rows][8].
 __global__ __launch_bounds__(256) void gather_mxfp8_kernel(const uint16_t* __restrict__ x,
                                                            const int32_t* __restrict__ inv,
                                                            uint8_t* __restrict__ rows,
                                                            uint8_t* __restrict__ scales, int h,
-                                                           int k) {
+                                                           int k, int sc_cm_rows) {
   const int t = blockIdx.x;
   const int nb = h / kMxBlock;
   int dst[16];
-  for (int j = 0; j < k; ++j) dst[j] = inv[(size_t)t * k + j];
+  if (!inv) k = 1;
+  for (int j = 0; j < k; ++j) dst[j] = inv ? inv[(size_t)t * k + j] : t;
   for (int b = threadIdx.x; b < nb; b += 256) {
     const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * h + (size_t)b * kMxBlock);
     float v[32];
@@ -189,7 +192,9 @@ __global__ __launch_bounds__(256) void gather_mxfp8_kernel(const uint16_t* __res
       uint4* d = reinterpret_cast<uint4*>(rows + (size_t)dst[j] * h + (size_t)b * kMxBlock);
       d[0] = lo;
       d[1] = hi;
-      scales[(size_t)dst[j] * nb + b] = (uint8_t)(s + 127);
+      const size_t so = sc_cm_rows > 0 ? ((size_t)(b >> 3) * sc_cm_rows + dst[j]) * 8 + (b & 7)
+                                       : (size_t)dst[j] * nb + b;
+      scales[so] = (uint8_t)(s + 127);
     }
   }
 }
@@ -223,7 +228,15 @@ hipError_t launch_gather_bf16(const uint16_t* x, const int32_t* inv, uint16_t* r
 
 hipError_t launch_gather_mxfp8(const uint16_t* x, const int32_t* inv, uint8_t* rows,
                                uint8_t* scales, int T, int h, int k, hipStream_t st) {
-  hipLaunchKernelGGL(gather_mxfp8_kernel, dim3(T), dim3(256), 0, st, x, inv, rows, scales, h, k);
+  hipLaunchKernelGGL(gather_mxfp8_kernel, dim3(T), dim3(256), 0, st, x, inv, rows, scales, h, k,
+                     0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_tokens_mxfp8(const uint16_t* x, uint8_t* codes, uint8_t* scales_cm,
+                                        int T, int h, hipStream_t st) {
+  hipLaunchKernelGGL(gather_mxfp8_kernel, dim3(T), dim3(256), 0, st, x, nullptr, codes,
+                     scales_cm, h, 1, T);
   return hipGetLastError();
 }
 
