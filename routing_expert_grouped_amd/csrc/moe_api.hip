@@ -126,7 +126,8 @@ moe_status check_router_shape(const moe_shape* s) {
 
 struct ForwardLayout {
   size_t logits, idx, w, counts, offsets, perm, inv, sched, rows, row_scales, ffn, out_rows;
-  size_t xf;  // the router's float32 copy of x: inside `rows` (free until the gather) if it fits
+  size_t xf;  // the router's float32 copies of x and W_r: inside `rows` (free until the gather)
+              // if they fit
   size_t shared_off, shared_ffn, shared_out, total;
   bool router;
 };
@@ -155,7 +156,7 @@ ForwardLayout forward_layout(const moe_shape* s, moe_dtype dt, bool router) {
   L.ffn = take(ffn_workspace_bytes((int)R, s->h, s->m, s->E_loc, mx));
   L.out_rows = take(R * s->h * 2);
   if (router) {
-    const size_t need = router_xf_bytes(s->T, s->h);
+    const size_t need = router_xf_bytes(s->T, s->h, s->E);
     L.xf = need <= R * s->h * (mx ? 1 : 2) ? L.rows : take(need);
   }
   if (s->m_shared > 0) {

@@ -94,11 +94,12 @@ inline bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
 // Router (moe_route_kernels.hip)
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias,
                                 float* logits, int T, int h, int E, hipStream_t st);
-// the same logits from x converted once to float32 and interleaved by 8 tokens into xf
-// (router_xf_bytes(T, h) bytes of scratch)
-size_t router_xf_bytes(int T, int h);
+// the same logits from x and the router matrix converted once to float32 and interleaved (x by
+// 8 tokens, the matrix by 8 columns), in router_xf_bytes(T, h, E) bytes of scratch
+size_t router_xf_bytes(int T, int h, int E);
 hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                                   float* logits, int T, int h, int E, float* xf, hipStream_t st);
+                                   float* logits, int T, int h, int E, float* scratch,
+                                   hipStream_t st);
 hipError_t launch_topk_softmax(const float* logits, int32_t* idx, float* w, int T, int E, int k,
                                hipStream_t st);
 

@@ -77,16 +77,31 @@ __global__ __launch_bounds__(256) void x_interleave_kernel(const uint16_t* __res
   d[1] = (f32x4_t){v[4], v[5], v[6], v[7]};
 }
 
-// The same logits, in the same order, from the interleaved float32 x: the 64 scalar operands of
-// a step of 8 columns are 256 contiguous bytes (scalar loads, no conversion on the scalar unit,
-// which otherwise issues as many instructions as the FMAs).
+// The router matrix as float32, 8 columns of every expert side by side: wi[v][e][0..7] =
+// w[e][8v .. 8v+7], [h/8][E][8]. One thread per (e, v); 32 contiguous bytes written per thread.
+__global__ __launch_bounds__(256) void w_interleave_kernel(const uint16_t* __restrict__ w, int E,
+                                                           int h, float* __restrict__ wi) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int v = blockIdx.y;
+  if (e >= E) return;
+  const uint4 x = *reinterpret_cast<const uint4*>(w + (size_t)e * h + 8 * v);
+  f32x4_t* d = reinterpret_cast<f32x4_t*>(wi + ((size_t)v * E + e) * 8);
+  d[0] = (f32x4_t){bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
+  d[1] = (f32x4_t){bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
+}
+
+// The same logits, in the same order, from the interleaved float32 x and router matrix:
+//  - the 64 scalar operands of a step of 8 columns are 256 contiguous bytes (scalar loads, no
+//    conversion on the scalar unit, which otherwise issues as many instructions as the FMAs);
+//  - a wave's router-matrix loads of a step are 64 experts x 32 bytes, contiguous (16 cache
+//    lines instead of one line per lane, which thrashed the vector L1: a lane's row is revisited
+//    only 8 steps later).
 __global__ __launch_bounds__(kRouterThreads) void router_logits_xf_kernel(
-    const float* __restrict__ xf, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ xf, const float* __restrict__ wi, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int h, int E) {
   const int e = blockIdx.y * kRouterThreads + threadIdx.x;
   const int t0 = blockIdx.x * kRouterTokens;
   const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
-  const uint4* wrow = reinterpret_cast<const uint4*>(w + (size_t)e_ld * h);
   const float* xg = xf + (size_t)blockIdx.x * h * kRouterTokens;
   float acc[kRouterTokens];
 #pragma unroll
@@ -94,9 +109,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_xf_kernel(
 
   const int nvec = h / 8;
   for (int v = 0; v < nvec; ++v) {
-    const uint4 wv = wrow[v];
-    const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                         bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+    const f32x4_t* wp = reinterpret_cast<const f32x4_t*>(wi + ((size_t)v * E + e_ld) * 8);
+    const f32x4_t w0 = wp[0], w1 = wp[1];
+    const float wf[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
     const float* xs = xg + (size_t)v * 8 * kRouterTokens;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -193,18 +208,25 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, con
   return hipGetLastError();
 }
 
-size_t router_xf_bytes(int T, int h) {
-  return (size_t)((T + kRouterTokens - 1) / kRouterTokens) * kRouterTokens * h * sizeof(float);
+size_t router_xf_bytes(int T, int h, int E) {
+  const size_t xf = (size_t)((T + kRouterTokens - 1) / kRouterTokens) * kRouterTokens * h * 4;
+  return align_up(xf) + (size_t)E * h * 4;
 }
 
 hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                                   float* logits, int T, int h, int E, float* xf, hipStream_t st) {
+                                   float* logits, int T, int h, int E, float* scratch,
+                                   hipStream_t st) {
   const int groups = (T + kRouterTokens - 1) / kRouterTokens;
+  float* xf = scratch;
+  float* wi = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(scratch) +
+                                       align_up((size_t)groups * kRouterTokens * h * 4));
   hipLaunchKernelGGL(x_interleave_kernel, dim3((h + 255) / 256, groups), dim3(256), 0, st, x, T, h,
                      xf);
+  hipLaunchKernelGGL(w_interleave_kernel, dim3((E + 255) / 256, h / 8), dim3(256), 0, st, w_router,
+                     E, h, wi);
   dim3 grid(groups, (E + kRouterThreads - 1) / kRouterThreads);
-  hipLaunchKernelGGL(router_logits_xf_kernel, grid, dim3(kRouterThreads), 0, st, xf, w_router,
-                     bias, logits, T, h, E);
+  hipLaunchKernelGGL(router_logits_xf_kernel, grid, dim3(kRouterThreads), 0, st, xf, wi, bias,
+                     logits, T, h, E);
   return hipGetLastError();
 }
 
