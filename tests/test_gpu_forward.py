@@ -1,5 +1,6 @@
 """GPU parity of moe_forward (the whole layer) on scaled-down versions of the five workloads:
-routing and schedule bit-exact, output within tolerance, and two runs bitwise identical."""
+routing and schedule bit-exact, output within tolerance, two runs bitwise identical, and the same
+bits as the separate entry points composed (route, permute, expert FFN, combine)."""
 import numpy as np
 import pytest
 
@@ -75,3 +76,47 @@ def test_forward_scaled_workloads(name):
     _, y1, _ = run_forward(G, wl, inp, weights, shared, y=y1)
     torch.cuda.synchronize()
     assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y1))
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv4pro", "qwen397", "kimi", "glm52"])
+def test_forward_equals_composed_entry_points(name):
+    """moe_forward (router on float32-staged operands, the gather done inside GEMM-1's loads, MXFP8
+    tokens quantised once) gives bitwise the y, logits and schedule of the separate entry points
+    moe_route -> moe_permute -> moe_expert_ffn (+ shared expert) -> moe_combine."""
+    G = require_gpu()
+    base = I.get(name)
+    wl = I.scaled(base, **SCALED[name]) if SCALED[name] else base
+    note(f"forward vs composed {wl.describe()}")
+    inp = I.make_inputs(wl, seed=3)
+    wts = [I.expert_weights(wl, e, seed=3) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    shared = None
+    if wl.m_shared:
+        shared = tuple(dev_bf16(v) for v in I.shared_weights(wl, seed=3))
+    sh, y, ws = run_forward(G, wl, inp, weights, shared)
+    v = G.moe_forward_views(sh, wl.dtype, ws)
+
+    x = dev_bf16(inp["x"])
+    prepared = G.moe_prepare_weights(sh, wl.dtype, *weights)
+    if wl.mode == "router":
+        logits, idx, gw = G.moe_route(sh, x, dev_bf16(inp["w_router"]),
+                                      None if inp["bias"] is None else dev(inp["bias"]))
+        assign, gate_w = idx.reshape(-1).contiguous(), gw.reshape(-1).contiguous()
+    else:
+        assign, gate_w = dev(inp["assign"]), dev(inp["assign_w"])
+    o = G.moe_permute(sh, wl.dtype, assign, x)
+    out_rows = G.moe_expert_ffn(sh, wl.dtype, o["rows"], o["row_scales"], o["offsets"], prepared)
+    shared_out = None
+    if shared is not None:
+        ssh = G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1)
+        sprep = G.moe_prepare_weights(ssh, "bf16", *shared)
+        soff = torch.tensor([0, wl.T], dtype=torch.int32, device=x.device)
+        shared_out = G.moe_expert_ffn(ssh, "bf16", x, None, soff, sprep)
+    y2 = G.moe_combine(sh, out_rows, o["inv"], gate_w, shared_out)
+    torch.cuda.synchronize()
+    if wl.mode == "router":
+        assert np.array_equal(v["logits"].cpu().numpy().view(np.uint32),
+                              logits.cpu().numpy().view(np.uint32))
+    for key in ("counts", "offsets", "perm", "inv"):
+        assert np.array_equal(v[key].cpu().numpy(), o[key].cpu().numpy()), key
+    assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))
