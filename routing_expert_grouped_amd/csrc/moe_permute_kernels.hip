@@ -9,7 +9,9 @@
 //   1. count:  per chunk of 256 assignments, a histogram over the local experts (LDS integer
 //              atomics; integer counts do not depend on their order);
 //   2. scan:   one exclusive scan over the (expert, chunk) matrix in expert-major order gives the
-//              first row of every (expert, chunk) pair, the expert offsets and counts;
+//              first row of every (expert, chunk) pair, the expert offsets and counts. It runs as
+//              a scan over each expert's chunks (one wave per expert, relative to the expert's
+//              first row) and a scan over the expert totals (one workgroup);
 //   3. rank:   each assignment's row = its (expert, chunk) base + the number of earlier
 //              assignments of the same expert in its chunk (wave ballots, then a prefix over the
 //              chunk's four waves), so rows inside an expert follow the assignment order and the
@@ -38,22 +40,38 @@ __global__ __launch_bounds__(kChunk) void sched_count_kernel(const int32_t* __re
   for (int e = tid; e < E_loc; e += kChunk) cc[(size_t)e * nchunks + blockIdx.x] = hist[e];
 }
 
-// Exclusive scan of n = E_loc * nchunks ints in place (cc -> base), one workgroup of 1024.
-__global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ cc, int E_loc,
-                                                          int nchunks,
-                                                          int32_t* __restrict__ counts,
+// Per expert e (one wave each): the exclusive prefix of its chunk counts, in place (cc ->
+// first row of (e, chunk) relative to the expert's first row), and its total.
+__global__ __launch_bounds__(64) void sched_expert_scan_kernel(int32_t* __restrict__ cc,
+                                                                int nchunks,
+                                                                int32_t* __restrict__ counts) {
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x;
+  int32_t* row = cc + (size_t)e * nchunks;
+  int run = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const int x = c < nchunks ? row[c] : 0;
+    int v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(v, off);
+      if (lane >= off) v += o;
+    }
+    if (c < nchunks) row[c] = run + v - x;
+    run += __shfl(v, 63);
+  }
+  if (lane == 0) counts[e] = run;
+}
+
+// Exclusive scan of the E_loc <= 1024 expert counts: offsets[0..E_loc], one workgroup of 1024.
+__global__ __launch_bounds__(1024) void sched_scan_kernel(const int32_t* __restrict__ counts,
+                                                          int E_loc,
                                                           int32_t* __restrict__ offsets) {
   __shared__ int wsum[16];
-  __shared__ int total_s;
   const int tid = threadIdx.x;
-  const int n = E_loc * nchunks;
-  const int per = (n + 1023) / 1024;
-  const int b0 = tid * per;
-  const int b1 = min(n, b0 + per);
-  int s = 0;
-  for (int i = b0; i < b1; ++i) s += cc[i];
-  // block exclusive scan of s
-  int v = s;
+  const int x = tid < E_loc ? counts[tid] : 0;
+  int v = x;
   const int lane = tid & 63, wid = tid >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -69,28 +87,17 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ 
       wsum[w] = run;
       run += t;
     }
-    total_s = run;
   }
   __syncthreads();
-  int run = v + wsum[wid] - s;  // exclusive prefix of this thread's segment
-  for (int i = b0; i < b1; ++i) {
-    const int c = cc[i];
-    cc[i] = run;
-    run += c;
-  }
-  __syncthreads();  // the block's global writes are visible to the block after the barrier
-  for (int e = tid; e < E_loc; e += 1024) {
-    const int o0 = cc[(size_t)e * nchunks];
-    const int o1 = (e + 1 < E_loc) ? cc[(size_t)(e + 1) * nchunks] : total_s;
-    offsets[e] = o0;
-    counts[e] = o1 - o0;
-  }
-  if (tid == 0) offsets[E_loc] = total_s;
+  const int incl = v + wsum[wid];
+  if (tid < E_loc) offsets[tid] = incl - x;
+  if (tid == E_loc - 1) offsets[E_loc] = incl;
 }
 
 __global__ __launch_bounds__(kChunk) void sched_rank_kernel(const int32_t* __restrict__ assign,
                                                             int R, int E_loc, int nchunks,
                                                             const int32_t* __restrict__ base,
+                                                            const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ inv) {
   extern __shared__ int wcnt[];  // [4][E_loc]: rows of expert e taken by each wave of the chunk
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(kChunk) void sched_rank_kernel(const int32_t* __res
   __syncthreads();
   if (a < R) {
     if (e >= 0) {
-      int r = base[(size_t)e * nchunks + blockIdx.x] + rank_w;
+      int r = offsets[e] + base[(size_t)e * nchunks + blockIdx.x] + rank_w;
       for (int w = 0; w < wid; ++w) r += wcnt[w * E_loc + e];
       perm[r] = a;
       inv[a] = r;
@@ -213,10 +220,10 @@ hipError_t launch_schedule(const int32_t* assign, int R, int E_loc, int32_t* cou
   int32_t* cc = reinterpret_cast<int32_t*>(ws);
   hipLaunchKernelGGL(sched_count_kernel, dim3(nchunks), dim3(kChunk), E_loc * sizeof(int), st,
                      assign, R, E_loc, nchunks, cc);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, st, cc, E_loc, nchunks, counts,
-                     offsets);
+  hipLaunchKernelGGL(sched_expert_scan_kernel, dim3(E_loc), dim3(64), 0, st, cc, nchunks, counts);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, st, counts, E_loc, offsets);
   hipLaunchKernelGGL(sched_rank_kernel, dim3(nchunks), dim3(kChunk), 4 * E_loc * sizeof(int), st,
-                     assign, R, E_loc, nchunks, cc, perm, inv);
+                     assign, R, E_loc, nchunks, cc, offsets, perm, inv);
   return hipGetLastError();
 }
 
