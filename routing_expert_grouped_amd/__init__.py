@@ -85,10 +85,19 @@ def moe_prepare_weights(shape: MoeShape, dtype, w_gate, w_up, w_down, prepared=N
     return prepared
 
 
+def moe_route_workspace_bytes(shape: MoeShape) -> int:
+    return load().moe_route_workspace_bytes(ctypes.byref(shape))
+
+
 def moe_route(shape: MoeShape, x, w_router, bias=None, logits=None, topk_idx=None, topk_w=None,
-              stream=None):
+              ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     dev = _dev(x)
+    if ws is None:
+        n = moe_route_workspace_bytes(shape)
+        if n == 0:
+            raise MoeError("moe_route_workspace_bytes", 1, "shape rejected")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
     logits = torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits
     topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
     topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
@@ -98,7 +107,7 @@ def moe_route(shape: MoeShape, x, w_router, bias=None, logits=None, topk_idx=Non
         _ptr(bias, "bias", torch.float32, E),
         _ptr(logits, "logits", torch.float32, T * E),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k),
-        _ptr(topk_w, "topk_w", torch.float32, T * k), _stream(stream)))
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(ws, "ws"), _stream(stream)))
     return logits, topk_idx, topk_w
 
 

@@ -18,7 +18,7 @@ MOE_BF16, MOE_MXFP8 = 0, 1
 EXPORTS = [
     "moe_status_string", "moe_abi_version",
     "moe_prepared_weight_bytes", "moe_prepare_weights",
-    "moe_route",
+    "moe_route_workspace_bytes", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
     "moe_combine",
@@ -72,7 +72,8 @@ def load() -> ctypes.CDLL:
         "moe_abi_version": (I, []),
         "moe_prepared_weight_bytes": (Z, [S, I]),
         "moe_prepare_weights": (I, [S, I, P, P, P, P, P]),
-        "moe_route": (I, [S, P, P, P, P, P, P, P]),
+        "moe_route_workspace_bytes": (Z, [S]),
+        "moe_route": (I, [S, P, P, P, P, P, P, P, P]),
         "moe_permute_workspace_bytes": (Z, [S]),
         "moe_permute": (I, [S, I, P, P, P, P, P, P, P, P, P, P]),
         "moe_expert_ffn_workspace_bytes": (Z, [S, I]),

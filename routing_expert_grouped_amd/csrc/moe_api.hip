@@ -206,16 +206,22 @@ moe_status moe_prepare_weights(const moe_shape* s, moe_dtype dt, const uint16_t*
                                            dt == MOE_MXFP8, as_stream(stream)));
 }
 
+size_t moe_route_workspace_bytes(const moe_shape* s) {
+  if (check_router_shape(s) != MOE_OK) return 0;
+  return router_xf_bytes(s->T, s->h, s->E);
+}
+
 moe_status moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
-                     const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                     const float* bias, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
                      void* stream) {
   const moe_status st = check_router_shape(s);
   if (st != MOE_OK) return st;
   if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_opt(bias) || !ok_ptr(logits) || !ok_ptr(topk_idx) ||
-      !ok_ptr(topk_w))
+      !ok_ptr(topk_w) || !ok_ptr(ws))
     return MOE_EINVAL;
   const hipStream_t hs = as_stream(stream);
-  hipError_t e = launch_router_logits(x, w_router, bias, logits, s->T, s->h, s->E, hs);
+  hipError_t e = launch_router_logits_xf(x, w_router, bias, logits, s->T, s->h, s->E,
+                                         reinterpret_cast<float*>(ws), hs);
   if (e == hipSuccess) e = launch_topk_softmax(logits, topk_idx, topk_w, s->T, s->E, s->k, hs);
   return hip_status(e);
 }

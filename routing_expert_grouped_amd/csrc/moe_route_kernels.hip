@@ -13,51 +13,12 @@ constexpr int kRouterThreads = 256;  // one expert per lane
 
 // logits[t, e] = (((0 + x[t,0] w[e,0]) + x[t,1] w[e,1]) + ...) + bias[e], float32, one fused
 // multiply-add per step. A bf16 x bf16 product is exact in float32, so each step rounds once and
-// the order is the written left-to-right one: no split over h, no tree.
+// the order is the written left-to-right one: no split over h, no tree. Bound by the float32 FMA
+// rate, 2*T*h*E flop.
 //
-// Layout: each lane owns one expert (its router row is contiguous in h and streamed 8 values per
-// 16-byte load); each workgroup owns kRouterTokens tokens whose x values are wave-uniform, so they
-// are fetched with scalar loads and fed to the FMAs as scalar operands. The work is bound by the
-// float32 FMA rate, 2*T*h*E flop.
-__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
-    float* __restrict__ logits, int T, int h, int E) {
-  const int e = blockIdx.y * kRouterThreads + threadIdx.x;
-  const int t0 = blockIdx.x * kRouterTokens;
-  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
-  const uint4* wrow = reinterpret_cast<const uint4*>(w + (size_t)e_ld * h);
-  const uint4* xrow[kRouterTokens];
-#pragma unroll
-  for (int tt = 0; tt < kRouterTokens; ++tt) {
-    int t = t0 + tt < T ? t0 + tt : T - 1;
-    xrow[tt] = reinterpret_cast<const uint4*>(x + (size_t)t * h);
-  }
-  float acc[kRouterTokens];
-#pragma unroll
-  for (int tt = 0; tt < kRouterTokens; ++tt) acc[tt] = 0.0f;
-
-  const int nvec = h / 8;
-  for (int v = 0; v < nvec; ++v) {
-    const uint4 wv = wrow[v];
-    const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                         bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
-#pragma unroll
-    for (int tt = 0; tt < kRouterTokens; ++tt) {
-      const uint4 xv = xrow[tt][v];
-      const float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                           bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[tt] = __builtin_fmaf(xf[q], wf[q], acc[tt]);
-    }
-  }
-  if (e < E) {
-    const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-    for (int tt = 0; tt < kRouterTokens; ++tt) {
-      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = bias ? acc[tt] + b : acc[tt];
-    }
-  }
-}
+// Layout: each lane owns one expert; each workgroup owns kRouterTokens tokens whose x values are
+// wave-uniform, so they are fetched with scalar loads and fed to the FMAs as scalar operands.
+// Both operands are first staged once as float32 (exact):
 
 // x as float32, 8 tokens interleaved: xf[g][i][j] = x[8g + j][i] (zeros past T), [ceil(T/8)][h][8].
 // One thread per (group g, column i); the 8 values it writes are 32 contiguous bytes.
@@ -199,14 +160,6 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 }
 
 }  // namespace
-
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                                float* logits, int T, int h, int E, hipStream_t st) {
-  dim3 grid((T + kRouterTokens - 1) / kRouterTokens, (E + kRouterThreads - 1) / kRouterThreads);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRouterThreads), 0, st, x, w_router, bias,
-                     logits, T, h, E);
-  return hipGetLastError();
-}
 
 size_t router_xf_bytes(int T, int h, int E) {
   const size_t xf = (size_t)((T + kRouterTokens - 1) / kRouterTokens) * kRouterTokens * h * 4;

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     L = lib.load()
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     for code in range(4):
         assert L.moe_status_string(code).decode().startswith("MOE_")
 
@@ -70,16 +70,19 @@ def test_route_validation(lib):
     L = lib.load()
     P = FAKE
     ok = _shape(lib)
-    assert L.moe_route(None, P, P, None, P, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(_shape(lib, k=9)), P, P, None, P, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(_shape(lib, E=8, E_loc=4)), P, P, None, P, P, P, None) == \
+    assert L.moe_route(None, P, P, None, P, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(_shape(lib, k=9)), P, P, None, P, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(_shape(lib, E=8, E_loc=4)), P, P, None, P, P, P, P, None) == \
         lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(ok), None, P, None, P, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(ok), P + 2, P, None, P, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(ok), P, P, P + 4, P, P, P, None) == lib.MOE_EINVAL
-    assert L.moe_route(ctypes.byref(_shape(lib, E=2000, E_loc=2000)), P, P, None, P, P, P,
+    assert L.moe_route(ctypes.byref(ok), None, P, None, P, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), P + 2, P, None, P, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), P, P, P + 4, P, P, P, P, None) == lib.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(ok), P, P, None, P, P, P, None, None) == lib.MOE_EINVAL  # ws
+    assert L.moe_route_workspace_bytes(ctypes.byref(ok)) > 0
+    assert L.moe_route_workspace_bytes(ctypes.byref(_shape(lib, k=9))) == 0
+    assert L.moe_route(ctypes.byref(_shape(lib, E=2000, E_loc=2000)), P, P, None, P, P, P, P,
                        None) == lib.MOE_EUNSUPPORTED
-    assert L.moe_route(ctypes.byref(_shape(lib, E=40, E_loc=40, k=17)), P, P, None, P, P, P,
+    assert L.moe_route(ctypes.byref(_shape(lib, E=40, E_loc=40, k=17)), P, P, None, P, P, P, P,
                        None) == lib.MOE_EUNSUPPORTED
 
 
