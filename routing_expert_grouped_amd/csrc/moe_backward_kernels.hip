@@ -185,14 +185,13 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
   __shared__ float tile[RBT][65];
   const int kk0 = blockIdx.y * RBT;
   if (kk0 >= koff[E_loc]) return;  // uniform: past the last segment
-  // the expert whose segment holds kk0: the largest e with koff[e] <= kk0
-  int lo = 0, hi = E_loc - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (koff[mid] <= kk0) lo = mid;
-    else hi = mid - 1;
-  }
-  const int e = lo;
+  // the expert whose segment holds kk0 (exactly one: koff[e] <= kk0 < koff[e+1]), found by the
+  // block's threads in parallel: one round of loads instead of a chain of dependent ones
+  __shared__ int e_s;
+  for (int i = threadIdx.x; i < E_loc; i += 256)
+    if (koff[i] <= kk0 && kk0 < koff[i + 1]) e_s = i;
+  __syncthreads();
+  const int e = e_s;
   const int kbase = koff[e];
   const int kpad = koff[e + 1] - kbase;
   const int q0 = kk0 - kbase;
@@ -202,19 +201,43 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
   const int tid = threadIdx.x;
   const int cq = (tid & 7) * 8;
 
-  for (int t = tid >> 3; t < RBT; t += 32) {
-    const int q = q0 + t;
+  // each thread fills rows t0 + 32 i of the tile (RBT / 32 of them): all their source indices
+  // are requested first, then all their loads, so a block waits for two memory round trips
+  // rather than two per row
+  constexpr int RPT = RBT / 32;
+  const int t0 = tid >> 3;
+  int src_row[RPT];  // routed row (or token for the gathered sources) of each row, -1: zero pad
+  float wt[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int q = q0 + t0 + 32 * i;
+    src_row[i] = q < n_e ? r0 + q : -1;
+    wt[i] = 1.0f;
+  }
+  if constexpr (SRC == kTrX || SRC == kTrDO) {
+    int a[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) a[i] = src_row[i] >= 0 ? perm[src_row[i]] : -1;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (a[i] >= 0) {
+        if constexpr (SRC == kTrDO) wt[i] = w[a[i]];
+        src_row[i] = a[i] / k;  // the token
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int t = t0 + 32 * i;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (q < n_e) {
-      const int r = r0 + q;
+    if (src_row[i] >= 0) {
+      const int r = src_row[i];
       if constexpr (SRC == kTrX || SRC == kTrDO) {
         const uint16_t* src = reinterpret_cast<const uint16_t*>(src_);
-        const int a = perm[r];
-        unpack8(*reinterpret_cast<const uint4*>(src + (size_t)(a / k) * C + c0 + cq), v);
+        unpack8(*reinterpret_cast<const uint4*>(src + (size_t)r * C + c0 + cq), v);
         if constexpr (SRC == kTrDO) {
-          const float wt = w[a];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] *= wt;
+          for (int j = 0; j < 8; ++j) v[j] *= wt[i];
         }
       } else if constexpr (SRC == kTrH) {
         const float* gu = reinterpret_cast<const float*>(src_) + (size_t)r * 2 * C;
@@ -225,23 +248,23 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
         const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gu + gcol + 32);
         const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gu + gcol + 36);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = g0[i] / (1.0f + expf(-g0[i])) * u0[i];
-          v[4 + i] = g1[i] / (1.0f + expf(-g1[i])) * u1[i];
+        for (int j = 0; j < 4; ++j) {
+          v[j] = g0[j] / (1.0f + expf(-g0[j])) * u0[j];
+          v[4 + j] = g1[j] / (1.0f + expf(-g1[j])) * u1[j];
         }
       } else {
-        const float* s = reinterpret_cast<const float*>(src_) + (size_t)r * C + c0 + cq;
-        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(s);
-        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(s + 4);
+        const float* sp = reinterpret_cast<const float*>(src_) + (size_t)r * C + c0 + cq;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(sp);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(sp + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = a0[i];
-          v[4 + i] = a1[i];
+        for (int j = 0; j < 4; ++j) {
+          v[j] = a0[j];
+          v[4 + j] = a1[j];
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[t][cq + i] = v[i];
+    for (int j = 0; j < 8; ++j) tile[t][cq + j] = v[j];
   }
   __syncthreads();
 

@@ -21,21 +21,31 @@ constexpr int kRouterThreads = 256;  // one expert per lane
 // Both operands are first staged once as float32 (exact):
 
 // x as float32, 8 tokens interleaved: xf[g][i][j] = x[8g + j][i] (zeros past T), [ceil(T/8)][h][8].
-// One thread per (group g, column i); the 8 values it writes are 32 contiguous bytes.
+// One thread per (group g, 8 columns): 8 16-byte loads (one per token), 256 contiguous bytes out.
 __global__ __launch_bounds__(256) void x_interleave_kernel(const uint16_t* __restrict__ x, int T,
                                                            int h, float* __restrict__ xf) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i8 = blockIdx.x * 256 + threadIdx.x;  // columns 8 i8 .. 8 i8 + 7
   const int g = blockIdx.y;
-  if (i >= h) return;
-  float v[kRouterTokens];
+  if (8 * i8 >= h) return;
+  uint4 raw[kRouterTokens];
 #pragma unroll
   for (int j = 0; j < kRouterTokens; ++j) {
     const int t = g * kRouterTokens + j;
-    v[j] = t < T ? bf16_to_f32(x[(size_t)t * h + i]) : 0.0f;
+    raw[j] = t < T ? *reinterpret_cast<const uint4*>(x + (size_t)t * h + 8 * i8)
+                   : make_uint4(0u, 0u, 0u, 0u);
   }
-  f32x4_t* d = reinterpret_cast<f32x4_t*>(xf + ((size_t)g * h + i) * kRouterTokens);
-  d[0] = (f32x4_t){v[0], v[1], v[2], v[3]};
-  d[1] = (f32x4_t){v[4], v[5], v[6], v[7]};
+  f32x4_t* d = reinterpret_cast<f32x4_t*>(xf + ((size_t)g * h + 8 * i8) * kRouterTokens);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float v[kRouterTokens];
+#pragma unroll
+    for (int j = 0; j < kRouterTokens; ++j) {
+      const uint32_t wd = c < 2 ? raw[j].x : c < 4 ? raw[j].y : c < 6 ? raw[j].z : raw[j].w;
+      v[j] = (c & 1) ? bf16_hi(wd) : bf16_lo(wd);
+    }
+    d[2 * c] = (f32x4_t){v[0], v[1], v[2], v[3]};
+    d[2 * c + 1] = (f32x4_t){v[4], v[5], v[6], v[7]};
+  }
 }
 
 // The router matrix as float32, 8 columns of every expert side by side: wi[v][e][0..7] =
@@ -173,8 +183,8 @@ hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, 
   float* xf = scratch;
   float* wi = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(scratch) +
                                        align_up((size_t)groups * kRouterTokens * h * 4));
-  hipLaunchKernelGGL(x_interleave_kernel, dim3((h + 255) / 256, groups), dim3(256), 0, st, x, T, h,
-                     xf);
+  hipLaunchKernelGGL(x_interleave_kernel, dim3((h / 8 + 255) / 256, groups), dim3(256), 0, st, x,
+                     T, h, xf);
   hipLaunchKernelGGL(w_interleave_kernel, dim3((E + 255) / 256, h / 8), dim3(256), 0, st, w_router,
                      E, h, wi);
   dim3 grid(groups, (E + kRouterThreads - 1) / kRouterThreads);
