@@ -33,5 +33,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_encode.restype = None
         L.oracle_mx_quantize_rows.argtypes = [P, Z, Z, P, P]
         L.oracle_mx_quantize_rows.restype = None
+        L.oracle_mx_roundtrip_axis.argtypes = [P, P, Z, Z, Z, P]
+        L.oracle_mx_roundtrip_axis.restype = None
         _lib = L
     return _lib

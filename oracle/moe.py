@@ -99,7 +99,7 @@ def route(x, w_router, bias, k):
 # ----------------------------------------------------------------------------------------------
 
 
-def schedule(assign: np.ndarray, n_experts: int):
+def schedule(assign: np.ndarray, n_experts: int, drop: bool = False):
     """Group the assignments by expert, keeping their order inside each expert.
 
     The Mixture-of-Kittens page's flowchart and Key claims describe a device-side schedule that
@@ -110,15 +110,21 @@ def schedule(assign: np.ndarray, n_experts: int):
       perm[r]    = the assignment held in routed row r (rows of e are offsets[e] .. offsets[e+1]-1,
                    assignments ascending inside each expert),
       inv[a]     = the row that holds assignment a (inv[perm[r]] == r).
+
+    Reading (the pages say nothing of expert ids outside the local range): with drop=True an
+    assignment whose expert id is outside [0, n_experts) gets no row and inv = -1, so perm holds
+    offsets[-1] <= R entries; with drop=False such an id is an error.
     """
     a = np.asarray(assign, dtype=np.int64).reshape(-1)
-    if a.size and (a.min() < 0 or a.max() >= n_experts):
+    valid = (a >= 0) & (a < n_experts)
+    if not drop and not valid.all():
         raise ValueError("expert id out of range")
-    counts = np.bincount(a, minlength=n_experts).astype(np.int32)
+    counts = np.bincount(a[valid], minlength=n_experts).astype(np.int32)
     offsets = np.zeros(n_experts + 1, dtype=np.int32)
     np.cumsum(counts, out=offsets[1:])
-    perm = np.argsort(a, kind="stable").astype(np.int32)
-    inv = np.empty_like(perm)
+    kept = np.nonzero(valid)[0]
+    perm = kept[np.argsort(a[kept], kind="stable")].astype(np.int32)
+    inv = np.full(a.size, -1, dtype=np.int32)
     inv[perm] = np.arange(perm.size, dtype=np.int32)
     return counts, offsets, perm, inv
 
@@ -188,7 +194,8 @@ def expert_outputs(A_rows: np.ndarray, offsets: np.ndarray, weights_of, mx: bool
 
 
 def combine(O: np.ndarray, inv: np.ndarray, w: np.ndarray, k: int, shared=None) -> np.ndarray:
-    """y[t] = S[t] + sum over j = 0..k-1 of w[t, j] * O[inv[t*k + j]] (S = 0 without a shared expert).
+    """y[t] = S[t] + sum over j = 0..k-1 of w[t, j] * O[inv[t*k + j]] (S = 0 without a shared expert),
+    skipping dropped assignments (inv = -1, see schedule).
 
     The Mixture-of-Kittens page stresses bitwise determinism through a fixed floating-point order;
     the result here is the plain weighted sum in float64, the GPU's fixed j-ascending float32 order
@@ -199,7 +206,8 @@ def combine(O: np.ndarray, inv: np.ndarray, w: np.ndarray, k: int, shared=None) 
     y = np.zeros((inv.shape[0], O.shape[1]), dtype=np.float64) if shared is None else \
         np.array(shared, dtype=np.float64, copy=True)
     for j in range(k):
-        y += w[:, j:j + 1] * O[inv[:, j]]
+        sel = inv[:, j] >= 0  # a dropped assignment (inv = -1) contributes nothing
+        y[sel] += w[sel, j:j + 1] * O[inv[sel, j]]
     return y
 
 
@@ -224,7 +232,7 @@ def layer_forward(wl, inp: dict, weights_of, shared_weights=None, keep: bool = F
     else:
         assign = inp["assign"]
         wflat = inp["assign_w"].astype(np.float64)
-    counts, offsets, perm, inv = schedule(assign, wl.E_loc)
+    counts, offsets, perm, inv = schedule(assign, wl.E_loc, drop=True)
     out.update(counts=counts, offsets=offsets, perm=perm, inv=inv)
     x64 = bf16_to_f64(inp["x"])
     A = gather_rows(x64, perm, wl.k)
@@ -240,9 +248,13 @@ def layer_forward(wl, inp: dict, weights_of, shared_weights=None, keep: bool = F
     return out
 
 
-def token_outputs(wl, inp: dict, tokens, weights_of, shared_weights=None) -> dict:
+def token_outputs(wl, inp: dict, tokens, weights_of, shared_weights=None, workers: int = 1) -> dict:
     """y[t] for a few tokens only. Each routed row depends only on its own token and expert, so a
-    token's output needs no other token's rows; used to check full-size runs on sampled tokens."""
+    token's output needs no other token's rows; used to check full-size runs on sampled tokens.
+
+    Experts are visited in ascending id order and their contributions added in that order;
+    workers > 1 computes the per-expert FFNs in a thread pool (the same values, added in the same
+    order). Expert ids outside [0, E_loc) contribute nothing (schedule's drop reading)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     x64 = bf16_to_f64(inp["x"][tokens])
     res = {"tokens": tokens}
@@ -258,12 +270,24 @@ def token_outputs(wl, inp: dict, tokens, weights_of, shared_weights=None) -> dic
     if shared_weights is not None:
         wg, wu, wd = (bf16_to_f64(v) for v in shared_weights)
         y += swiglu_ffn(x64, wg, wu, wd, mx=False)
-    for e in np.unique(idx):
-        wg, wu, wd = (bf16_to_f64(v) for v in weights_of(int(e)))
+    experts = [int(e) for e in np.unique(idx) if 0 <= e < wl.E_loc]
+
+    def expert_rows(e):
+        wg, wu, wd = (bf16_to_f64(v) for v in weights_of(e))
         ti, jj = np.nonzero(idx == e)
-        o = swiglu_ffn(x64[ti], wg, wu, wd, mx=mx)
-        # a token can hold the same expert in two slots (expert shares): accumulate unbuffered
-        np.add.at(y, ti, w[ti, jj][:, None] * o)
+        return ti, jj, swiglu_ffn(x64[ti], wg, wu, wd, mx=mx)
+
+    if workers > 1 and len(experts) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            parts = ex.map(expert_rows, experts)  # results come back in submission order
+            for ti, jj, o in parts:
+                # a token can hold the same expert in two slots (expert shares): unbuffered add
+                np.add.at(y, ti, w[ti, jj][:, None] * o)
+    else:
+        for e in experts:
+            ti, jj, o = expert_rows(e)
+            np.add.at(y, ti, w[ti, jj][:, None] * o)
     res["y"] = y
     return res
 

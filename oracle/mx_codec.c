@@ -69,3 +69,43 @@ void oracle_mx_quantize_rows(const double* v, size_t nrows, size_t ncols, uint8_
     }
   }
 }
+
+/* The value each element takes after MX quantisation along one axis: v viewed as
+ * [outer][L][inner] (L % 32 == 0), blocks of 32 consecutive positions along L for every (outer,
+ * inner); out[i] = 2^s * value(code). The value of a code comes straight from its bit fields:
+ * exponent field 0 gives man * 2^-9, else (1 + man / 8) * 2^(ex - 7). amax is a scratch array of
+ * `inner` doubles. */
+static double e4m3_value(uint8_t c) {
+  const int ex = (c >> 3) & 0xF, man = c & 0x7;
+  const double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);
+  return (c & 0x80) ? -mag : mag;
+}
+
+void oracle_mx_roundtrip_axis(const double* v, double* out, size_t outer, size_t L, size_t inner,
+                              double* amax) {
+  for (size_t o = 0; o < outer; ++o) {
+    for (size_t b = 0; b < L / 32; ++b) {
+      const double* blk = v + (o * L + 32 * b) * inner;
+      double* dst = out + (o * L + 32 * b) * inner;
+      for (size_t i = 0; i < inner; ++i) amax[i] = 0.0;
+      for (int q = 0; q < 32; ++q)
+        for (size_t i = 0; i < inner; ++i) amax[i] = fmax(amax[i], fabs(blk[q * inner + i]));
+      for (size_t i = 0; i < inner; ++i) { /* the block exponent s, kept in amax[i] */
+        int s = -127;
+        if (amax[i] > 0.0) {
+          int ex;
+          frexp(amax[i], &ex);
+          s = ex - 1 - 8;
+          if (s < -127) s = -127;
+          if (s > 127) s = 127;
+        }
+        amax[i] = (double)s;
+      }
+      for (int q = 0; q < 32; ++q)
+        for (size_t i = 0; i < inner; ++i) {
+          const int s = (int)amax[i];
+          dst[q * inner + i] = ldexp(e4m3_value(e4m3_encode_one(ldexp(blk[q * inner + i], -s))), s);
+        }
+    }
+  }
+}

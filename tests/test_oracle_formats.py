@@ -154,3 +154,19 @@ def test_mx_error_bound_and_axis(rng):
     assert np.array_equal(F.mx_roundtrip(v.T, axis=0), deq.T)
     with pytest.raises(ValueError):
         F.mx_quantize(np.zeros((2, 33)))
+
+
+def test_mx_roundtrip_equals_table_decode_of_quantize(rng):
+    """The C round trip (in-place blocks, code values from the bit fields) equals decoding the
+    codes mx_quantize gives through the OFP8-pinned value table, bit for bit, on every axis,
+    including zeros of both signs, saturation, subnormal E4M3 results and extreme scales."""
+    for shape, axis in [((64, 96), 0), ((64, 96), 1), ((6, 64, 40), 1), ((32,), 0),
+                        ((5, 3, 64), -1), ((2, 32, 3, 5), 1)]:
+        v = rng.standard_normal(shape) * np.exp2(rng.integers(-150, 128, size=shape))
+        v.flat[::7] = 0.0
+        v.flat[::11] *= -0.0
+        v.flat[::13] = 460.0 * np.exp2(rng.integers(-20, 20))
+        got = F.mx_roundtrip(v, axis)
+        q, s = F.mx_quantize(v, axis)
+        want = F.mx_dequantize(q, s, axis)
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (shape, axis)

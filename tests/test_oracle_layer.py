@@ -177,3 +177,27 @@ def test_backward_vs_finite_differences():
             return wmod
         fd = (loss(x0, wmod_factory(eps)) - loss(x0, wmod_factory(-eps))) / (2 * eps)
         assert abs(fd - dW[e][which][p, q]) <= 1e-6 * max(1.0, abs(fd)), (e, which)
+
+
+def test_dropped_assignments_contribute_nothing():
+    """Reading: assignments with an expert id outside [0, E_loc) are dropped. The layer then equals
+    the same layer with those slots sent to a valid expert at gate weight 0 (0 * O = 0), and the
+    sampled-token path agrees with the whole layer (also with a thread pool over experts)."""
+    wl = I.scaled(I.get("dsv4pro"), T=40, h=64, m=64, name="drop")
+    inp = I.make_inputs(wl, seed=4)
+    wts = [I.expert_weights(wl, e, seed=4) for e in range(wl.E_loc)]
+    bad = np.zeros(wl.R, bool)
+    bad[::5] = True
+    dropped = dict(inp)
+    dropped["assign"] = np.where(bad, np.int32(wl.E_loc + 2), inp["assign"]).astype(np.int32)
+    zeroed = dict(inp)
+    zeroed["assign_w"] = np.where(bad, np.float32(0.0), inp["assign_w"]).astype(np.float32)
+    a = M.layer_forward(wl, dropped, lambda e: wts[e])
+    b = M.layer_forward(wl, zeroed, lambda e: wts[e])
+    assert np.array_equal(a["y"], b["y"])
+    assert a["offsets"][-1] == wl.R - bad.sum() and np.all(a["inv"][bad] == -1)
+    toks = np.arange(wl.T)
+    t1 = M.token_outputs(wl, dropped, toks, lambda e: wts[e])
+    t4 = M.token_outputs(wl, dropped, toks, lambda e: wts[e], workers=4)
+    assert np.array_equal(t1["y"], t4["y"])
+    assert np.allclose(t1["y"], a["y"], rtol=1e-12, atol=1e-12)

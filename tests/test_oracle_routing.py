@@ -74,9 +74,13 @@ def test_router_fixed_order_is_left_to_right():
     w = f32_to_bf16(np.ones((1, 3), np.float32))
     assert M.router_logits_fixed_order(x, w)[0, 0] == 0.0
     assert M.router_logits_f64(x, w)[0, 0] == 1.0
-    # right to left would give (-2**24 + 1) + 2**24 = 0 too; the middle-first order gives 1:
+    # right to left would give (-2**24 + 1) + 2**24 = 1 (-2**24 + 1 is exact in float32), so the 0
+    # above pins the left-to-right order; putting the 1 first gives 0 again, since 1 + 2**24
+    # rounds to 2**24 before -2**24 is added:
     x2 = f32_to_bf16(np.array([[1.0, 2.0 ** 24, -2.0 ** 24]], np.float32))
-    assert M.router_logits_fixed_order(x2, w)[0, 0] == 0.0  # (1 + 2**24) rounds to 2**24 first
+    assert M.router_logits_fixed_order(x2, w)[0, 0] == 0.0
+    x3 = f32_to_bf16(np.array([[-2.0 ** 24, 1.0, 2.0 ** 24]], np.float32))
+    assert M.router_logits_fixed_order(x3, w)[0, 0] == 1.0  # (-2**24 + 1) is exact, then + 2**24
 
 
 def test_router_fixed_order_vs_f64_bound(rng):
@@ -117,3 +121,19 @@ def test_schedule_each_token_expert_pair_once(rng):
     assert len(pairs) == T * k
     with pytest.raises(ValueError):
         M.schedule(np.array([0, 5]), 5)
+
+
+def test_schedule_drops_out_of_range_ids(rng):
+    """Reading: an expert id outside [0, E) gets no row and inv = -1; the kept assignments are
+    scheduled exactly as if the dropped ones were not there (brute force with Python sorted)."""
+    E, R = 7, 500
+    a = rng.integers(-3, E + 3, size=R).astype(np.int32)
+    a[:5] = [E, -1, 0x7FFFFFFF, 3, 3]
+    counts, offsets, perm, inv = M.schedule(a, E, drop=True)
+    valid = [q for q in range(R) if 0 <= a[q] < E]
+    assert counts.sum() == len(valid) == offsets[-1] == perm.size
+    assert perm.tolist() == sorted(valid, key=lambda q: (a[q], q))
+    assert all(inv[q] == -1 for q in range(R) if not 0 <= a[q] < E)
+    assert np.array_equal(inv[perm], np.arange(perm.size))
+    with pytest.raises(ValueError):
+        M.schedule(a, E)
