@@ -4,13 +4,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one moe_forward of the whole hot path over one batch of seeded synthetic inputs
-(expert shares: schedule, gather, grouped SwiGLU GEMMs, combine; full layers: router and top-k
-first). The default workload is the DeepSeek-V4-Pro-shaped expert share of one GPU at expert
-parallelism 64 (2,048 source tokens, 6 local experts, top-6, h = 7168, m = 3072, BF16).
+(router, top-k, schedule, per-token MX quantisation, grouped SwiGLU GEMMs, combine; expert shares
+skip the router). The default workload is the largest one that fits one GPU: the GLM-5.2-shaped
+full layer (8,192 tokens, 256 experts, top-8, h = 6144, m = 2048, MXFP8, the pages' default
+precision). The other four workloads are measured too, with fewer steps, as extra keys.
 
 Inputs live in HBM before the timed region starts. The K timed steps run back to back between two
 device synchronisations; each step records HIP events at its stage boundaries on the library's
-stream, which gives every kernel's duration live. One JSON line is printed.
+stream, which gives every kernel's duration live. After the timed region, a few more steps each
+preceded by a 1 GiB write give the bandwidth stages' GB/s with the 256 MB last-level cache flushed.
+One JSON line is printed.
 
 The CPU baseline times the oracle (oracle/, float64 NumPy) on a bounded sample of the same
 workload's tokens on the host cores.
@@ -26,6 +29,8 @@ import time
 
 import numpy as np
 
+import moe_inputs as I_
+
 METRIC = "MoE layer fwd tokens/s on 1 GPU + grouped-GEMM % MFMA peak (BF16/MXFP8)"
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}  # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
@@ -36,14 +41,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv4pro")
+    ap.add_argument("--workload", default="glm52")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
-                    help="tokens of the oracle's timed sample (0 disables the CPU baseline)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=-1,
+                    help="tokens of the oracle's timed sample (0 disables the CPU baseline; "
+                         "default: every token of an expert share, 32 of a router layer)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much wall time has run")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward timing of workloads that define one")
+    ap.add_argument("--others", default="tiny,dsv4pro,qwen397,kimi",
+                    help="further workloads measured as extra keys ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=10)
+    ap.add_argument("--flush-steps", type=int, default=3,
+                    help="steps after a 1 GiB cache flush for the bandwidth stages' GB/s")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
@@ -116,31 +127,73 @@ def measured_traffic(workload: str):
     return int(kv["gemm1_bytes_per_launch"])
 
 
-def cpu_baseline(wl, inp, weights_host, shared_host, n_tokens: int, min_seconds: float) -> dict:
-    """Times the oracle on the first n_tokens tokens, repeating the pass until at least
-    min_seconds of wall time have run (a sample that is the whole workload takes only a few
-    seconds on a many-core host), and reports tokens per second over all passes."""
-    from oracle import moe as M  # the oracle is the baseline leg only
+def host_info() -> dict:
+    """The host the CPU baseline ran on: usable cores, CPU model, NumPy's BLAS build."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
     except Exception:  # noqa: BLE001
-        threads = 1
-    tokens = np.arange(min(n_tokens, wl.T))
+        pass
+    return {"cores": cores, "cpu_model": model, "blas": blas, "numpy": np.__version__}
+
+
+def cpu_baseline(wl, inp, weights_of, shared_host, n_tokens: int, min_seconds: float) -> dict:
+    """Times the oracle as it stands (oracle.moe.token_outputs: float64 NumPy, one expert at a
+    time) on a bounded sample of the workload's tokens, repeating the pass until at least
+    min_seconds of wall time have run, and reports tokens per second over all passes.
+
+    An expert share (6 experts) is run on every token with BLAS on all usable cores. A router layer
+    is run on n_tokens sampled tokens with the oracle's per-expert thread pool on all usable cores
+    (one BLAS thread each): its sample touches most experts, and each expert's weights are
+    MX-quantised once per pass, work that a whole-layer pass would spread over all of that
+    expert's rows."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe as M  # the oracle is the baseline leg only
+    info = host_info()
+    cores = info["cores"]
+    rng = np.random.default_rng(0)
+    if wl.mode == "share":
+        tokens = np.arange(min(n_tokens, wl.T))
+    else:
+        tokens = np.sort(rng.choice(wl.T, min(n_tokens, wl.T), replace=False))
+    workers = 1 if wl.mode == "share" else cores
+    n_exp = len({int(e) for e in (M.route(inp["x"][tokens], inp["w_router"], inp["bias"],
+                                          wl.k)[1] if wl.mode == "router"
+                                  else inp["assign"].reshape(-1, wl.k)[tokens]).reshape(-1)
+                 if 0 <= e < wl.E_loc})
     passes = 0
     t0 = time.perf_counter()
-    while True:
-        M.token_outputs(wl, inp, tokens, weights_host.__getitem__, shared_host)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": round(passes * len(tokens) / dt, 3), "unit": "tokens/s", "cores": int(threads),
+    with threadpool_limits(1 if workers > 1 else cores):
+        while True:
+            M.token_outputs(wl, inp, tokens, weights_of, shared_host, workers=workers)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    what = ("every token" if len(tokens) == wl.T else
+            f"{len(tokens)} of {wl.T} tokens (seeded sample)")
+    return {"value": round(passes * len(tokens) / dt, 3), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"first {len(tokens)} of {wl.T} tokens of the same workload through "
-                      f"oracle.moe.token_outputs (float64 NumPy, routing + every selected "
-                      f"expert's SwiGLU FFN + combine), {passes} pass(es), {dt:.1f} s wall"}
+            "sample": f"{what} of the same workload through oracle.moe.token_outputs (float64 "
+                      f"NumPy: routing, every selected expert's SwiGLU FFN with its MX steps, "
+                      f"combine), touching {n_exp} of {wl.E_loc} experts, {passes} pass(es), "
+                      f"{dt:.1f} s wall, "
+                      + ("BLAS on all cores" if workers == 1 else
+                         f"{workers} expert workers with one BLAS thread each"),
+            "host": info}
 
 
 def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
@@ -193,6 +246,130 @@ def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
             "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
 
 
+def expert_roofline(wl, counts, g1_ms: float, g2_ms: float) -> dict:
+    """The grouped GEMMs against the per-expert roofline: each expert e with n_e routed rows takes
+    at least max(FLOP_e / MFMA peak, bytes_e / HBM peak), summed over experts. GEMM-1: FLOP_e =
+    4 h m n_e, bytes_e = W1 (2 h m elements) + n_e input rows (h) + H written (n_e m); GEMM-2:
+    FLOP_e = 2 h m n_e, bytes_e = W2 (h m) + H read (n_e m) + O written (n_e h, bf16). Element
+    sizes: E4M3 1 byte + one scale byte per 32 (MXFP8), bf16 2 bytes."""
+    mx = wl.dtype == "mxfp8"
+    be = (1 + 1 / 32) if mx else 2.0
+    pf = PEAK_TFLOPS[wl.dtype] * 1e12
+    bw = PEAK_HBM_GBS * 1e9
+    h, m = wl.h, wl.m
+    n = np.asarray(counts, np.float64)
+    n = n[n > 0]
+    t1 = np.maximum(4 * h * m * n / pf, (2 * h * m * be + n * h * be + n * m * be) / bw).sum()
+    t2 = np.maximum(2 * h * m * n / pf, (h * m * be + n * m * be + n * h * 2) / bw).sum()
+    return {"gemm1_bound_ms": round(t1 * 1e3, 4), "gemm2_bound_ms": round(t2 * 1e3, 4),
+            "gemm1_frac": round(t1 * 1e3 / g1_ms, 4), "gemm2_frac": round(t2 * 1e3 / g2_ms, 4),
+            "gemms_frac": round((t1 + t2) * 1e3 / (g1_ms + g2_ms), 4)}
+
+
+class Setup:
+    """A workload's inputs, weights and prepared weights on the device."""
+
+    def __init__(self, G, wl, dev, seed):
+        import torch
+
+        self.wl, self.dev = wl, dev
+        self.inp = I_.make_inputs(wl, seed=seed)
+        self.x = self.bf16(self.inp["x"])
+        self.w = I_.torch_expert_weights(wl, dev, seed=seed)
+        self.sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared)
+        self.prepared = G.moe_prepare_weights(self.sh, wl.dtype, *self.w)
+        self.shared_w = self.shared_prep = None
+        if wl.m_shared:
+            self.shared_w = I_.torch_shared_weights(wl, dev, seed=seed)
+            ssh = G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1)
+            self.shared_prep = G.moe_prepare_weights(ssh, "bf16", *self.shared_w)
+        self.kw = {}
+        if wl.mode == "router":
+            self.kw["w_router"] = self.bf16(self.inp["w_router"])
+            self.kw["bias"] = (None if self.inp["bias"] is None
+                               else torch.from_numpy(self.inp["bias"]).to(dev))
+        else:
+            self.kw["assign"] = torch.from_numpy(self.inp["assign"]).to(dev)
+            self.kw["assign_w"] = torch.from_numpy(self.inp["assign_w"]).to(dev)
+        self.y = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(G.moe_forward_workspace_bytes(self.sh, wl.dtype), dtype=torch.uint8,
+                              device=dev)
+
+    def bf16(self, a):
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(
+            torch.bfloat16)
+
+
+def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> dict:
+    """Times `steps` back-to-back forwards (after `warmup`), every stage with HIP events; then
+    `flush_steps` forwards each preceded by a 1 GiB write (outside the stage events) for the
+    bandwidth stages' GB/s with the last-level cache flushed."""
+    import torch
+
+    wl = S.wl
+
+    def step(ev):
+        G.moe_forward_profiled(S.sh, wl.dtype, S.x, S.prepared, ev, shared_prepared=S.shared_prep,
+                               y=S.y, ws=S.ws, **S.kw)
+
+    events = [G.HipEvents() for _ in range(steps)]
+    warm_ev = G.HipEvents()
+    for _ in range(warmup):
+        step(warm_ev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    stages = {k: 0.0 for k in G.STAGES}
+    for ev in events:
+        for k, v in ev.stage_ms().items():
+            stages[k] += v / steps
+    flushed = {k: 0.0 for k in G.STAGES}
+    if flush_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=S.dev)
+        fev = [G.HipEvents() for _ in range(flush_steps)]
+        for ev in fev:
+            scratch.fill_(1)
+            step(ev)
+        torch.cuda.synchronize()
+        for ev in fev:
+            for k, v in ev.stage_ms().items():
+                flushed[k] += v / flush_steps
+            ev.close()
+        del scratch
+    for ev in events + [warm_ev]:
+        ev.close()
+    counts = G.moe_forward_views(S.sh, wl.dtype, S.ws)["counts"].cpu().numpy()
+    fl = layer_flops(wl)
+    by = stage_bytes(wl)
+    peak = PEAK_TFLOPS[wl.dtype]
+    g1_ms, g2_ms = stages["gemm1_gate_up_swiglu"], stages["gemm2_down"]
+
+    def gbs(name, st):
+        ms = st[name]
+        return round(by[name] / (ms * 1e-3) / 1e9, 1) if ms > 0 and by[name] else None
+
+    return {
+        "tokens_per_s": round(wl.T / (ms_per_step * 1e-3), 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "gemm1_tflops": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12, 1),
+        "gemm1_mfma_frac": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12 / peak, 4),
+        "grouped_gemm_mfma_frac": round((fl["gemm1"] + fl["gemm2"]) / ((g1_ms + g2_ms) * 1e-3)
+                                        / 1e12 / peak, 4),
+        "expert_roofline": expert_roofline(wl, counts, g1_ms, g2_ms),
+        "layer_tflops": round(fl["total"] / (ms_per_step * 1e-3) / 1e12, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stages_gbs": {k: gbs(k, stages) for k in ("gather", "combine", "topk")},
+        "stages_gbs_flushed": ({k: gbs(k, flushed) for k in ("gather", "combine", "topk")}
+                               if flush_steps > 0 else None),
+        "router_tflops": (round(fl["router"] / (stages["router_logits"] * 1e-3) / 1e12, 1)
+                          if fl["router"] and stages["router_logits"] > 0 else None),
+    }
+
+
 def main() -> int:
     args = parse()
     if args.copy_calibration:
@@ -206,109 +383,69 @@ def main() -> int:
 
     import torch
 
-    import moe_inputs as I
     import routing_expert_grouped_amd as G
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    wl = I.get(args.workload)
+    wl = I_.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = I.make_inputs(wl, seed=args.seed)
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    x = bf16(inp["x"])
-    wg, wu, wd = I.torch_expert_weights(wl, dev, seed=args.seed)
-    sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared)
-    prepared = G.moe_prepare_weights(sh, wl.dtype, wg, wu, wd)
-    shared_prep = None
-    shared_w = None
-    if wl.m_shared:
-        shared_w = I.torch_shared_weights(wl, dev, seed=args.seed)
-        ssh = G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1)
-        shared_prep = G.moe_prepare_weights(ssh, "bf16", *shared_w)
-    kw = {}
-    if wl.mode == "router":
-        kw["w_router"] = bf16(inp["w_router"])
-        kw["bias"] = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev)
-    else:
-        kw["assign"] = torch.from_numpy(inp["assign"]).to(dev)
-        kw["assign_w"] = torch.from_numpy(inp["assign_w"]).to(dev)
-    y = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(G.moe_forward_workspace_bytes(sh, wl.dtype), dtype=torch.uint8, device=dev)
-    events = [G.HipEvents() for _ in range(args.steps)]
-    warm_ev = G.HipEvents()
-
-    def step(ev):
-        G.moe_forward_profiled(sh, wl.dtype, x, prepared, ev, shared_prepared=shared_prep, y=y,
-                               ws=ws, **kw)
-
-    for _ in range(args.warmup):
-        step(warm_ev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    stages = {k: 0.0 for k in G.STAGES}
-    for ev in events:
-        for k, v in ev.stage_ms().items():
-            stages[k] += v / args.steps
-    for ev in events + [warm_ev]:
-        ev.close()
-
-    fl = layer_flops(wl)
-    by = stage_bytes(wl)
-    peak = PEAK_TFLOPS[wl.dtype]
-    g1_ms = stages["gemm1_gate_up_swiglu"]
-    g2_ms = stages["gemm2_down"]
-    g1_tf = fl["gemm1"] / (g1_ms * 1e-3) / 1e12
-    gemm_tf = (fl["gemm1"] + fl["gemm2"]) / ((g1_ms + g2_ms) * 1e-3) / 1e12
-    tokens_per_s = wl.T / (ms_per_step * 1e-3)
-
-    def gbs(name):
-        ms = stages[name]
-        return round(by[name] / (ms * 1e-3) / 1e9, 1) if ms > 0 and by[name] else None
+    S = Setup(G, wl, dev, args.seed)
+    r = measure_forward(G, S, args.steps, args.warmup, args.flush_steps)
 
     backward = None
     if wl.backward and not args.no_backward:
-        backward = time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args)
+        backward = time_backward(G, wl, S.sh, S.x, *S.w, S.prepared, S.kw, S.inp, args)
 
     baseline = None
-    if args.cpu_sample_tokens > 0:
+    n_cpu = args.cpu_sample_tokens
+    if n_cpu < 0:
+        n_cpu = wl.T if wl.mode == "share" else 32
+    if n_cpu > 0:
         def host_bits(t):
             return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-        class HostWeights(dict):
-            """Expert weights copied to the host on first use (all of them up front for an
-            expert share, which holds only a few experts)."""
+        cache = {}
 
-            def __missing__(self, e):
-                self[e] = tuple(host_bits(t[e]) for t in (wg, wu, wd))
-                return self[e]
+        def weights_of(e):
+            """Expert weights copied to the host (kept for the few experts of a share)."""
+            if e in cache:
+                return cache[e]
+            v = tuple(host_bits(t[e]) for t in S.w)
+            if wl.mode == "share":
+                cache[e] = v
+            return v
 
-        host = HostWeights()
         if wl.mode == "share":
             for e in range(wl.E_loc):
-                host[e]
-        sh_host = tuple(host_bits(t) for t in shared_w) if shared_w is not None else None
-        baseline = cpu_baseline(wl, inp, host, sh_host, args.cpu_sample_tokens,
-                                    args.cpu_min_seconds)
+                weights_of(e)
+        sh_host = tuple(host_bits(t) for t in S.shared_w) if S.shared_w is not None else None
+        baseline = cpu_baseline(wl, S.inp, weights_of, sh_host, n_cpu, args.cpu_min_seconds)
 
+    others = {}
+    for name in [n for n in args.others.split(",") if n]:
+        w2 = I_.get(name)
+        if w2.name == wl.name:
+            continue
+        S2 = Setup(G, w2, dev, args.seed)
+        o = measure_forward(G, S2, args.other_steps, 2, 0)
+        others[w2.name] = {k: o[k] for k in ("tokens_per_s", "ms_per_step", "gemm1_mfma_frac",
+                                             "grouped_gemm_mfma_frac", "expert_roofline",
+                                             "stages_ms")}
+        others[w2.name]["dtype"] = w2.dtype
+        del S2
+        torch.cuda.empty_cache()
+
+    peak = PEAK_TFLOPS[wl.dtype]
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -318,13 +455,17 @@ def main() -> int:
                    "E_loc": wl.E_loc, "k": wl.k, "routed_rows": wl.T * wl.k,
                    "mode": wl.mode, "m_shared": wl.m_shared},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM-1 (gate/up + SwiGLU epilogue)",
-                     "achieved": round(g1_tf, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(g1_tf / peak, 4), "traffic": measured_traffic(wl.name)},
-        "grouped_gemm_mfma_frac": round(gemm_tf / peak, 4),
-        "layer_tflops": round(fl["total"] / (ms_per_step * 1e-3) / 1e12, 1),
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-        "stages_gbs": {k: gbs(k) for k in ("gather", "combine", "topk")},
+                     "achieved": r["gemm1_tflops"], "peak": peak, "unit": "TFLOP/s",
+                     "frac": r["gemm1_mfma_frac"], "traffic": measured_traffic(wl.name)},
+        "expert_roofline": r["expert_roofline"],
+        "grouped_gemm_mfma_frac": r["grouped_gemm_mfma_frac"],
+        "layer_tflops": r["layer_tflops"],
+        "router_tflops": r["router_tflops"],
+        "stages_ms": r["stages_ms"],
+        "stages_gbs": r["stages_gbs"],
+        "stages_gbs_flushed": r["stages_gbs_flushed"],
         "cpu_baseline": baseline,
+        "other_workloads": others,
     }
     if backward is not None:
         out["backward"] = backward

@@ -15,13 +15,14 @@ from typing import Optional
 
 import torch
 
-from ._lib import (BWD_STAGES, MOE_BF16, MOE_BWD_PROFILE_EVENTS, MOE_MXFP8, MOE_PROFILE_EVENTS,
-                   STAGES, MoeError, MoeForwardViews, MoeShape, check, load)
+from ._lib import (BWD_STAGES, MOE_BF16, MOE_BWD_PROFILE_EVENTS, MOE_MXFP8,
+                   MOE_PERMUTE_STATIC_SCRATCH_BYTES, MOE_PROFILE_EVENTS, STAGES, MoeError,
+                   MoeForwardViews, MoeShape, check, load)
 
 __all__ = [
     "MOE_BF16", "MOE_MXFP8", "MoeError", "make_shape", "dtype_code",
     "moe_prepared_weight_bytes", "moe_prepare_weights", "moe_route", "moe_permute_workspace_bytes",
-    "moe_permute", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
+    "moe_permute", "moe_permute_static", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
@@ -42,10 +43,19 @@ def dtype_code(dtype) -> int:
     raise ValueError(f"unknown expert dtype {dtype!r}")
 
 
-def _stream(stream) -> int:
+def _stream_obj(stream):
+    """The torch stream the call enqueues on (None: the current stream; a raw hipStream_t handle
+    is wrapped). Buffers the binding allocates are allocated on it, so the caching allocator does
+    not hand them out again while that stream's kernels still use them."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _stream(stream) -> int:
+    return _stream_obj(stream).cuda_stream
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None):
@@ -57,6 +67,19 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] 
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _buf(t: Optional[torch.Tensor], name: str, nbytes: int):
+    """Pointer of a caller-owned byte buffer (workspace, saved state, prepared weights) that must
+    hold at least nbytes bytes: a smaller one would be written past its end by the kernels."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous CUDA tensor")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, the shape needs {nbytes}")
     return t.data_ptr()
 
 
@@ -73,15 +96,17 @@ def moe_prepare_weights(shape: MoeShape, dtype, w_gate, w_up, w_down, prepared=N
     n = moe_prepared_weight_bytes(shape, dt)
     if n == 0:
         raise MoeError("moe_prepared_weight_bytes", 1, "shape rejected")
+    st = _stream_obj(stream)
     if prepared is None:
-        prepared = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
+        with torch.cuda.stream(st):
+            prepared = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
     e, h, m = shape.E_loc, shape.h, shape.m
     check("moe_prepare_weights", load().moe_prepare_weights(
         ctypes.byref(shape), dt,
         _ptr(w_gate, "w_gate", torch.bfloat16, e * h * m),
         _ptr(w_up, "w_up", torch.bfloat16, e * h * m),
         _ptr(w_down, "w_down", torch.bfloat16, e * m * h),
-        _ptr(prepared, "prepared", torch.uint8, n), _stream(stream)))
+        _ptr(prepared, "prepared", torch.uint8, n), st.cuda_stream))
     return prepared
 
 
@@ -93,21 +118,23 @@ def moe_route(shape: MoeShape, x, w_router, bias=None, logits=None, topk_idx=Non
               ws=None, stream=None):
     T, E, k = shape.T, shape.E, shape.k
     dev = _dev(x)
-    if ws is None:
-        n = moe_route_workspace_bytes(shape)
-        if n == 0:
-            raise MoeError("moe_route_workspace_bytes", 1, "shape rejected")
-        ws = torch.empty(n, dtype=torch.uint8, device=dev)
-    logits = torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits
-    topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
-    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    n = moe_route_workspace_bytes(shape)
+    if n == 0:
+        raise MoeError("moe_route_workspace_bytes", 1, "shape rejected")
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+        logits = torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None \
+            else topk_idx
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
     check("moe_route", load().moe_route(
         ctypes.byref(shape), _ptr(x, "x", torch.bfloat16, T * shape.h),
         _ptr(w_router, "w_router", torch.bfloat16, E * shape.h),
         _ptr(bias, "bias", torch.float32, E),
         _ptr(logits, "logits", torch.float32, T * E),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k),
-        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(ws, "ws"), _stream(stream)))
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _buf(ws, "ws", n), st.cuda_stream))
     return logits, topk_idx, topk_w
 
 
@@ -121,27 +148,53 @@ def moe_permute(shape: MoeShape, dtype, assign, x, out: Optional[dict] = None, w
     T, h, k, E_loc = shape.T, shape.h, shape.k, shape.E_loc
     R = T * k
     dev = _dev(x)
-    o = dict(out or {})
-    o.setdefault("counts", torch.empty(E_loc, dtype=torch.int32, device=dev))
-    o.setdefault("offsets", torch.empty(E_loc + 1, dtype=torch.int32, device=dev))
-    o.setdefault("perm", torch.empty(R, dtype=torch.int32, device=dev))
-    o.setdefault("inv", torch.empty(R, dtype=torch.int32, device=dev))
-    if dt == MOE_MXFP8:
-        o.setdefault("rows", torch.empty(R, h, dtype=torch.uint8, device=dev))
-        o.setdefault("row_scales", torch.empty(R, h // 32, dtype=torch.uint8, device=dev))
-    else:
-        o.setdefault("rows", torch.empty(R, h, dtype=torch.bfloat16, device=dev))
-        o.setdefault("row_scales", None)
+    mx = dt == MOE_MXFP8
     nws = moe_permute_workspace_bytes(shape)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if ws is None else ws
+    if nws == 0:
+        raise MoeError("moe_permute_workspace_bytes", 1, "shape rejected")
+    st = _stream_obj(stream)
+    o = dict(out or {})
+    with torch.cuda.stream(st):
+        o.setdefault("counts", torch.empty(E_loc, dtype=torch.int32, device=dev))
+        o.setdefault("offsets", torch.empty(E_loc + 1, dtype=torch.int32, device=dev))
+        o.setdefault("perm", torch.empty(R, dtype=torch.int32, device=dev))
+        o.setdefault("inv", torch.empty(R, dtype=torch.int32, device=dev))
+        if mx:
+            o.setdefault("rows", torch.empty(R, h, dtype=torch.uint8, device=dev))
+            o.setdefault("row_scales", torch.empty(R, h // 32, dtype=torch.uint8, device=dev))
+        else:
+            o.setdefault("rows", torch.empty(R, h, dtype=torch.bfloat16, device=dev))
+            o.setdefault("row_scales", None)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if ws is None else ws
     check("moe_permute", load().moe_permute(
         ctypes.byref(shape), dt, _ptr(assign, "assign", torch.int32, R),
         _ptr(x, "x", torch.bfloat16, T * h), _ptr(o["counts"], "counts", torch.int32, E_loc),
         _ptr(o["offsets"], "offsets", torch.int32, E_loc + 1),
         _ptr(o["perm"], "perm", torch.int32, R), _ptr(o["inv"], "inv", torch.int32, R),
-        _ptr(o["rows"], "rows"), _ptr(o["row_scales"], "row_scales"), _ptr(ws, "ws"),
-        _stream(stream)))
+        _ptr(o["rows"], "rows", torch.uint8 if mx else torch.bfloat16, R * h),
+        _ptr(o["row_scales"], "row_scales", torch.uint8, R * (h // 32)) if mx else None,
+        _buf(ws, "ws", nws), st.cuda_stream))
     return o
+
+
+def moe_permute_static(shape: MoeShape, dtype, assign, x, out: dict, stream=None) -> dict:
+    """moe_permute with the schedule's scratch in the library's static per-GPU array (the C call
+    allocates nothing). Every output buffer is the caller's: out holds counts, offsets, perm, inv,
+    rows (and row_scales for MXFP8), as moe_permute returns them. Calls that overlap in time on
+    one GPU share that array and race."""
+    dt = dtype_code(dtype)
+    T, h, k, E_loc = shape.T, shape.h, shape.k, shape.E_loc
+    R = T * k
+    mx = dt == MOE_MXFP8
+    check("moe_permute_static", load().moe_permute_static(
+        ctypes.byref(shape), dt, _ptr(assign, "assign", torch.int32, R),
+        _ptr(x, "x", torch.bfloat16, T * h), _ptr(out["counts"], "counts", torch.int32, E_loc),
+        _ptr(out["offsets"], "offsets", torch.int32, E_loc + 1),
+        _ptr(out["perm"], "perm", torch.int32, R), _ptr(out["inv"], "inv", torch.int32, R),
+        _ptr(out["rows"], "rows", torch.uint8 if mx else torch.bfloat16, R * h),
+        _ptr(out["row_scales"], "row_scales", torch.uint8, R * (h // 32)) if mx else None,
+        _stream(stream)))
+    return out
 
 
 def moe_expert_ffn_workspace_bytes(shape: MoeShape, dtype) -> int:
@@ -151,30 +204,36 @@ def moe_expert_ffn_workspace_bytes(shape: MoeShape, dtype) -> int:
 def moe_expert_ffn(shape: MoeShape, dtype, rows, row_scales, offsets, prepared, out_rows=None,
                    ws=None, stream=None):
     dt = dtype_code(dtype)
-    R = shape.T * shape.k
+    R, h = shape.T * shape.k, shape.h
+    mx = dt == MOE_MXFP8
     dev = _dev(rows)
-    out_rows = torch.empty(R, shape.h, dtype=torch.bfloat16, device=dev) if out_rows is None \
-        else out_rows
     n = moe_expert_ffn_workspace_bytes(shape, dt)
     if n == 0:
         raise MoeError("moe_expert_ffn_workspace_bytes", 1, "shape rejected")
-    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        out_rows = torch.empty(R, h, dtype=torch.bfloat16, device=dev) if out_rows is None \
+            else out_rows
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
     check("moe_expert_ffn", load().moe_expert_ffn(
-        ctypes.byref(shape), dt, _ptr(rows, "rows"), _ptr(row_scales, "row_scales"),
-        _ptr(offsets, "offsets", torch.int32, shape.E_loc + 1), _ptr(prepared, "prepared"),
-        _ptr(out_rows, "out_rows", torch.bfloat16, R * shape.h), _ptr(ws, "ws"),
-        _stream(stream)))
+        ctypes.byref(shape), dt, _ptr(rows, "rows", torch.uint8 if mx else torch.bfloat16, R * h),
+        _ptr(row_scales, "row_scales", torch.uint8, R * (h // 32)) if mx else None,
+        _ptr(offsets, "offsets", torch.int32, shape.E_loc + 1),
+        _buf(prepared, "prepared", moe_prepared_weight_bytes(shape, dt)),
+        _ptr(out_rows, "out_rows", torch.bfloat16, R * h), _buf(ws, "ws", n), st.cuda_stream))
     return out_rows
 
 
 def moe_combine(shape: MoeShape, out_rows, inv, topk_w, shared_out=None, y=None, stream=None):
     T, h, k = shape.T, shape.h, shape.k
-    y = torch.empty(T, h, dtype=torch.bfloat16, device=_dev(out_rows)) if y is None else y
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        y = torch.empty(T, h, dtype=torch.bfloat16, device=_dev(out_rows)) if y is None else y
     check("moe_combine", load().moe_combine(
-        ctypes.byref(shape), _ptr(out_rows, "out_rows", torch.bfloat16),
+        ctypes.byref(shape), _ptr(out_rows, "out_rows", torch.bfloat16, T * k * h),
         _ptr(inv, "inv", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(shared_out, "shared_out", torch.bfloat16, T * h),
-        _ptr(y, "y", torch.bfloat16, T * h), _stream(stream)))
+        _ptr(y, "y", torch.bfloat16, T * h), st.cuda_stream))
     return y
 
 
@@ -182,25 +241,46 @@ def moe_forward_workspace_bytes(shape: MoeShape, dtype) -> int:
     return load().moe_forward_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
 
 
+def _forward_args(shape, dtype, x, prepared, w_router, bias, assign, assign_w, shared_prepared,
+                  y, ws, saved, stream):
+    """Checked argument list of moe_forward / moe_forward_profiled (without events and stream),
+    and the buffers the call writes."""
+    dt = dtype_code(dtype)
+    T, h, k, E = shape.T, shape.h, shape.k, shape.E
+    dev = _dev(x)
+    n = moe_forward_workspace_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_forward_workspace_bytes", 1, "shape rejected")
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    nsaved = moe_saved_bytes(shape, dt) if saved is not None else 0
+    if saved is not None and nsaved == 0:
+        raise MoeError("moe_saved_bytes", 2, "shape has no backward")
+    nshared = 0
+    if shared_prepared is not None:
+        nshared = moe_prepared_weight_bytes(make_shape(T, h, shape.m_shared, 1, 1, 1), MOE_BF16)
+    args = [ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h),
+            _ptr(w_router, "w_router", torch.bfloat16, E * h),
+            _ptr(bias, "bias", torch.float32, E),
+            _ptr(assign, "assign", torch.int32, T * k),
+            _ptr(assign_w, "assign_w", torch.float32, T * k),
+            _buf(prepared, "prepared", moe_prepared_weight_bytes(shape, dt)),
+            _buf(shared_prepared, "shared_prepared", nshared),
+            _ptr(y, "y", torch.bfloat16, T * h), _buf(saved, "saved", nsaved),
+            _buf(ws, "ws", n)]
+    return args, y, ws, st
+
+
 def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, assign=None,
                 assign_w=None, shared_prepared=None, y=None, ws=None, saved=None, stream=None):
     """The whole layer. Returns (y, ws); moe_forward_views(shape, dtype, ws) exposes the
     intermediates left in ws. saved: a moe_saved_bytes() uint8 tensor that receives what
     moe_backward needs, or None."""
-    dt = dtype_code(dtype)
-    T, h, k = shape.T, shape.h, shape.k
-    dev = _dev(x)
-    y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
-    n = moe_forward_workspace_bytes(shape, dt)
-    if n == 0:
-        raise MoeError("moe_forward_workspace_bytes", 1, "shape rejected")
-    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
-    check("moe_forward", load().moe_forward(
-        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h), _ptr(w_router, "w_router"),
-        _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
-        _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
-        _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
-        _ptr(saved, "saved", torch.uint8), _ptr(ws, "ws"), _stream(stream)))
+    args, y, ws, st = _forward_args(shape, dtype, x, prepared, w_router, bias, assign, assign_w,
+                                    shared_prepared, y, ws, saved, stream)
+    check("moe_forward", load().moe_forward(*args, st.cuda_stream))
     return y, ws
 
 
@@ -248,19 +328,13 @@ def moe_forward_profiled(shape: MoeShape, dtype, x, prepared, events: HipEvents,
                          bias=None, assign=None, assign_w=None, shared_prepared=None, y=None,
                          ws=None, saved=None, stream=None):
     """moe_forward plus HIP events at the stage boundaries (events.stage_ms() afterwards)."""
-    dt = dtype_code(dtype)
-    T, h, k = shape.T, shape.h, shape.k
-    dev = _dev(x)
-    y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
-    n = moe_forward_workspace_bytes(shape, dt)
-    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    if events.n != MOE_PROFILE_EVENTS:
+        raise ValueError(f"events: {events.n} handles, moe_forward_profiled records "
+                         f"{MOE_PROFILE_EVENTS}")
+    args, y, ws, st = _forward_args(shape, dtype, x, prepared, w_router, bias, assign, assign_w,
+                                    shared_prepared, y, ws, saved, stream)
     check("moe_forward_profiled", load().moe_forward_profiled(
-        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h), _ptr(w_router, "w_router"),
-        _ptr(bias, "bias", torch.float32), _ptr(assign, "assign", torch.int32, T * k),
-        _ptr(assign_w, "assign_w", torch.float32, T * k), _ptr(prepared, "prepared"),
-        _ptr(shared_prepared, "shared_prepared"), _ptr(y, "y", torch.bfloat16, T * h),
-        _ptr(saved, "saved", torch.uint8), _ptr(ws, "ws"),
-        ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
+        *args, ctypes.cast(events.handles, ctypes.c_void_p), st.cuda_stream))
     return y, ws
 
 
@@ -268,9 +342,9 @@ def moe_forward_views(shape: MoeShape, dtype, ws) -> dict:
     """Tensors viewing the intermediates moe_forward leaves in ws (None where absent)."""
     dt = dtype_code(dtype)
     v = MoeForwardViews()
-    check("moe_forward_views", load().moe_forward_views(ctypes.byref(shape), dt,
-                                                         ctypes.c_void_p(ws.data_ptr()),
-                                                         ctypes.byref(v)))
+    check("moe_forward_views", load().moe_forward_views(
+        ctypes.byref(shape), dt, ctypes.c_void_p(_buf(ws, "ws", moe_forward_workspace_bytes(
+            shape, dt))), ctypes.byref(v)))
     T, h, k, E, E_loc = shape.T, shape.h, shape.k, shape.E, shape.E_loc
     R = T * k
     base = ws.data_ptr()
@@ -312,15 +386,17 @@ def moe_prepare_bwd_weights(shape: MoeShape, dtype, w_gate, w_up, w_down, prepar
     n = moe_prepared_bwd_weight_bytes(shape, dt)
     if n == 0:
         raise MoeError("moe_prepared_bwd_weight_bytes", 2, "shape rejected")
+    st = _stream_obj(stream)
     if prepared_bwd is None:
-        prepared_bwd = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
+        with torch.cuda.stream(st):
+            prepared_bwd = torch.empty(n, dtype=torch.uint8, device=_dev(w_gate))
     e, h, m = shape.E_loc, shape.h, shape.m
     check("moe_prepare_bwd_weights", load().moe_prepare_bwd_weights(
         ctypes.byref(shape), dt,
         _ptr(w_gate, "w_gate", torch.bfloat16, e * h * m),
         _ptr(w_up, "w_up", torch.bfloat16, e * h * m),
         _ptr(w_down, "w_down", torch.bfloat16, e * m * h),
-        _ptr(prepared_bwd, "prepared_bwd", torch.uint8, n), _stream(stream)))
+        _ptr(prepared_bwd, "prepared_bwd", torch.uint8, n), st.cuda_stream))
     return prepared_bwd
 
 
@@ -328,33 +404,38 @@ def moe_backward_workspace_bytes(shape: MoeShape, dtype) -> int:
     return load().moe_backward_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
 
 
-def _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws):
+def _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws, stream):
     dt = dtype_code(dtype)
     T, h, m, E_loc = shape.T, shape.h, shape.m, shape.E_loc
     dev = _dev(x)
-    dx = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if dx is None else dx
     wdt = torch.float32 if dw_fp32 else torch.bfloat16
-    if dw is None:
-        dw = (torch.empty(E_loc, h, m, dtype=wdt, device=dev),
-              torch.empty(E_loc, h, m, dtype=wdt, device=dev),
-              torch.empty(E_loc, m, h, dtype=wdt, device=dev))
     n = moe_backward_workspace_bytes(shape, dt)
     if n == 0:
         raise MoeError("moe_backward_workspace_bytes", 2, "shape rejected")
-    ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        dx = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if dx is None else dx
+        if dw is None:
+            dw = (torch.empty(E_loc, h, m, dtype=wdt, device=dev),
+                  torch.empty(E_loc, h, m, dtype=wdt, device=dev),
+                  torch.empty(E_loc, m, h, dtype=wdt, device=dev))
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
     args = [ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h),
-            _ptr(dy, "dy", torch.bfloat16, T * h), _ptr(saved, "saved", torch.uint8),
-            _ptr(prepared_bwd, "prepared_bwd", torch.uint8), _ptr(dx, "dx", torch.bfloat16, T * h),
+            _ptr(dy, "dy", torch.bfloat16, T * h),
+            _buf(saved, "saved", moe_saved_bytes(shape, dt)),
+            _buf(prepared_bwd, "prepared_bwd", moe_prepared_bwd_weight_bytes(shape, dt)),
+            _ptr(dx, "dx", torch.bfloat16, T * h),
             _ptr(dw[0], "dw_gate", wdt, E_loc * h * m), _ptr(dw[1], "dw_up", wdt, E_loc * h * m),
-            _ptr(dw[2], "dw_down", wdt, E_loc * m * h), 1 if dw_fp32 else 0, _ptr(ws, "ws")]
-    return args, dx, dw, ws
+            _ptr(dw[2], "dw_down", wdt, E_loc * m * h), 1 if dw_fp32 else 0, _buf(ws, "ws", n)]
+    return args, dx, dw, ws, st
 
 
 def moe_backward(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, dx=None, dw=None,
                  dw_fp32: bool = True, ws=None, stream=None):
     """Backward of the expert path. Returns (dx, (dw_gate, dw_up, dw_down), ws)."""
-    args, dx, dw, ws = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws)
-    check("moe_backward", load().moe_backward(*args, _stream(stream)))
+    args, dx, dw, ws, st = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw,
+                                          dw_fp32, ws, stream)
+    check("moe_backward", load().moe_backward(*args, st.cuda_stream))
     return dx, dw, ws
 
 
@@ -362,7 +443,11 @@ def moe_backward_profiled(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, ev
                           dx=None, dw=None, dw_fp32: bool = True, ws=None, stream=None):
     """moe_backward plus HIP events at its stage boundaries (events.stage_ms() afterwards; create
     the events with HipEvents(MOE_BWD_PROFILE_EVENTS, BWD_STAGES))."""
-    args, dx, dw, ws = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw, dw_fp32, ws)
+    if events.n != MOE_BWD_PROFILE_EVENTS:
+        raise ValueError(f"events: {events.n} handles, moe_backward_profiled records "
+                         f"{MOE_BWD_PROFILE_EVENTS}")
+    args, dx, dw, ws, st = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw,
+                                          dw_fp32, ws, stream)
     check("moe_backward_profiled", load().moe_backward_profiled(
-        *args, ctypes.cast(events.handles, ctypes.c_void_p), _stream(stream)))
+        *args, ctypes.cast(events.handles, ctypes.c_void_p), st.cuda_stream))
     return dx, dw, ws

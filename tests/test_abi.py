@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     L = lib.load()
-    assert L.moe_abi_version() == 3
-    for code in range(4):
+    assert L.moe_abi_version() == 4
+    for code in range(5):
         assert L.moe_status_string(code).decode().startswith("MOE_")
 
 
@@ -166,3 +166,58 @@ def test_backward_sizes_and_validation(lib):
         lib.MOE_EINVAL  # no events
     assert L.moe_prepare_bwd_weights(ctypes.byref(_shape(lib, h=384)), 0, P, P, P, P, None) == \
         lib.MOE_EUNSUPPORTED
+
+
+def test_binding_buffer_checks_without_gpu():
+    """The binding's pointer checks, on stand-in tensors (no GPU needed): a byte buffer smaller
+    than the shape's size query is refused, as are wrong dtypes and element counts."""
+    import pytest as _pt
+    torch = _pt.importorskip("torch")
+    import routing_expert_grouped_amd as G
+
+    class Fake:
+        is_cuda = True
+
+        def __init__(self, n, dtype=torch.uint8, contiguous=True):
+            self.n, self.dtype, self.c = n, dtype, contiguous
+
+        def is_contiguous(self):
+            return self.c
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return torch.empty(0, dtype=self.dtype).element_size()
+
+        def data_ptr(self):
+            return 4096
+
+    assert G._buf(Fake(1000), "ws", 1000) == 4096
+    assert G._buf(Fake(250, torch.float32), "ws", 1000) == 4096
+    assert G._buf(None, "ws", 1000) is None
+    with _pt.raises(ValueError, match="ws: 999 bytes"):
+        G._buf(Fake(999), "ws", 1000)
+    with _pt.raises(ValueError, match="contiguous"):
+        G._buf(Fake(1000, contiguous=False), "ws", 10)
+    with _pt.raises(ValueError, match="dtype"):
+        G._ptr(Fake(8, torch.float32), "bias", torch.bfloat16, 8)
+    with _pt.raises(ValueError, match="elements"):
+        G._ptr(Fake(7, torch.float32), "bias", torch.float32, 8)
+
+
+def test_permute_static_rejects_shapes_beyond_its_scratch(lib):
+    """moe_permute_static checks the schedule's scratch size against the static array on the host
+    and returns MOE_ENOSCRATCH before touching the GPU (and EINVAL for null pointers first)."""
+    L = lib.load()
+    big = _shape(lib, T=70000, k=8, h=256, m=128, E=1024, E_loc=1024)
+    need = L.moe_permute_workspace_bytes(ctypes.byref(big))
+    assert need > lib.MOE_PERMUTE_STATIC_SCRATCH_BYTES
+    args = [FAKE] * 8
+    assert L.moe_permute_static(ctypes.byref(big), 0, *args, None, None) == lib.MOE_ENOSCRATCH
+    small = _shape(lib)
+    assert L.moe_permute_workspace_bytes(ctypes.byref(small)) <= \
+        lib.MOE_PERMUTE_STATIC_SCRATCH_BYTES
+    assert L.moe_permute_static(ctypes.byref(small), 0, None, *args[1:], None, None) == \
+        lib.MOE_EINVAL
+    assert "static buffer" in L.moe_status_string(lib.MOE_ENOSCRATCH).decode()

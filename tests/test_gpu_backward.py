@@ -12,7 +12,7 @@ from tests._gpu_helpers import (BF16_TOL, MX_TOL, dev, dev_bf16, host_f64_from_b
 
 pytestmark = pytest.mark.gpu
 
-PER_EXPERT_BOUND = 0.1
+PER_EXPERT_BOUND = 3e-2  # the MXFP8 bar, per expert as well as over the whole tensor
 
 CASES = {
     # router layers
@@ -91,9 +91,7 @@ def _check(wl, inp, wts, got):
             else:
                 worst = max(worst, normwise_err(g[e], ref[e]))
         note(f"  {name} normwise error {err:.3e} (worst expert {worst:.3e})")
-        # the bar is on the whole tensor; each expert on its own only has to be far from the ~1 a
-        # wrong segment or layout gives: an expert of ~30 rows sums too few terms to average out
-        # the odd E4M3 code that float32 and float64 round differently
+        # every expert on its own within the MXFP8 bar too (a wrong segment or layout gives ~1)
         assert err <= tol and worst <= PER_EXPERT_BOUND, name
 
 

@@ -120,3 +120,87 @@ def test_forward_equals_composed_entry_points(name):
     for key in ("counts", "offsets", "perm", "inv"):
         assert np.array_equal(v[key].cpu().numpy(), o[key].cpu().numpy()), key
     assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_dropped_assignments_forward_and_backward(dtype):
+    """Assignments whose expert id is outside [0, E_loc) are dropped (the library's documented
+    reading): inv = -1, no row, offsets[E_loc] = the number of valid ids, and y, dX and dW equal
+    the oracle's layer with those slots ignored. Exercises the schedule, the gather inside GEMM-1,
+    the combine, the un-combine, the transposes and the un-permute on a partly filled row buffer."""
+    G = require_gpu()
+    wl = I.Workload(name="drop", T=160, h=512, m=256, E=384, k=4, E_loc=5, dtype=dtype,
+                    mode="share", zipf_s=1.0, backward=True)
+    inp = I.make_inputs(wl, seed=9)
+    bad = np.zeros(wl.R, bool)
+    bad[3::7] = True
+    ids = np.array([wl.E_loc, -1, 0x7FFFFFFF, wl.E_loc + 100], np.int32)
+    inp["assign"] = np.where(bad, ids[np.arange(wl.R) % 4], inp["assign"]).astype(np.int32)
+    note(f"dropped assignments {wl.describe()}: {int(bad.sum())} of {wl.R} dropped")
+    wts = [I.expert_weights(wl, e, seed=9) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc)
+    x = dev_bf16(inp["x"])
+    o = G.moe_permute(sh, dtype, dev(inp["assign"]), x)
+    counts, offsets, perm, inv = M.schedule(inp["assign"], wl.E_loc, drop=True)
+    assert offsets[-1] == wl.R - bad.sum()
+    assert np.array_equal(o["counts"].cpu().numpy(), counts)
+    assert np.array_equal(o["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(o["perm"].cpu().numpy()[:offsets[-1]], perm)
+    assert np.array_equal(o["inv"].cpu().numpy(), inv)
+    prepared = G.moe_prepare_weights(sh, dtype, *weights)
+    saved = torch.empty(G.moe_saved_bytes(sh, dtype), dtype=torch.uint8, device="cuda")
+    y = poisoned((wl.T, wl.h), torch.bfloat16)
+    y, _ = G.moe_forward(sh, dtype, x, prepared, assign=dev(inp["assign"]),
+                         assign_w=dev(inp["assign_w"]), y=y, saved=saved)
+    pbwd = G.moe_prepare_bwd_weights(sh, dtype, *weights)
+    dx = poisoned((wl.T, wl.h), torch.bfloat16)
+    dx, dw, _ = G.moe_backward(sh, dtype, x, dev_bf16(inp["dy"]), saved, pbwd, dx=dx)
+    torch.cuda.synchronize()
+    fwd = M.layer_forward(wl, inp, lambda e: wts[e], keep=True)
+    tol = MX_TOL if dtype == "mxfp8" else BF16_TOL
+    err = normwise_err(host_f64_from_bf16(y), fwd["y"])
+    note(f"  y normwise error {err:.3e}")
+    assert err <= tol
+    dX, dW = M.layer_backward(wl, inp, fwd, lambda e: wts[e])
+    err = normwise_err(host_f64_from_bf16(dx), dX)
+    note(f"  dX normwise error {err:.3e}")
+    assert err <= tol
+    for i, nm in enumerate(("dW_gate", "dW_up", "dW_down")):
+        ref = np.stack([dW[e][i] for e in range(wl.E_loc)])
+        err = normwise_err(dw[i].cpu().numpy().astype(np.float64), ref)
+        note(f"  {nm} normwise error {err:.3e}")
+        assert err <= tol, nm
+
+
+def test_undersized_buffers_are_rejected_before_any_launch():
+    """The binding refuses a workspace, saved state or prepared-weight buffer smaller than the
+    size query for the shape (it would be written past its end), and a router matrix or bias of
+    the wrong size, with ValueError and nothing enqueued."""
+    G = require_gpu()
+    wl = I.scaled(I.get("glm52"), T=64, h=512, m=256, E=16, E_loc=16)
+    inp = I.make_inputs(wl, seed=0)
+    wts = [I.expert_weights(wl, e) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    sh = G.make_shape(wl.T, wl.h, wl.m, wl.E, wl.k, wl.E_loc)
+    prepared = G.moe_prepare_weights(sh, wl.dtype, *weights)
+    x, wr, b = dev_bf16(inp["x"]), dev_bf16(inp["w_router"]), dev(inp["bias"])
+    nws = G.moe_forward_workspace_bytes(sh, wl.dtype)
+    small = torch.empty(nws - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="ws"):
+        G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr, bias=b, ws=small)
+    with pytest.raises(ValueError, match="saved"):
+        G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr, bias=b,
+                      saved=torch.empty(1024, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError, match="prepared"):
+        G.moe_forward(sh, wl.dtype, x, prepared[:-1], w_router=wr, bias=b)
+    with pytest.raises(ValueError, match="w_router"):
+        G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr[:-1], bias=b)
+    with pytest.raises(ValueError, match="bias"):
+        G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr, bias=b[:-1])
+    with pytest.raises(ValueError, match="ws"):
+        G.moe_route(sh, x, wr, b, ws=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    y, _ = G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr, bias=b)  # the right sizes run
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()

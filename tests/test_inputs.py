@@ -64,3 +64,28 @@ def test_glm52_hot_set_receives_half_of_routed_rows():
     idx = M.topk(logits, wl.k)
     share = np.isin(idx, hot).mean()
     assert 0.495 <= share <= 0.505, share
+
+
+def test_cover_tokens_hits_every_tile():
+    """The full-size tests' token choice: every M tile of every expert at every tile height, and
+    every expert's first and last row, has a routed row of a chosen token (checked by brute
+    force on a router-shaped schedule with a hot set and empty experts)."""
+    from oracle import moe as M
+    from tests._sampling import TILE_HEIGHTS, cover_tokens
+    rng = np.random.default_rng(2)
+    T, E, k = 3000, 40, 4
+    l = rng.standard_normal((T, E))
+    l[:, :4] += 2.5  # a few hot experts with many tiles
+    l[:, 30:] -= 50.0  # some experts that receive nothing
+    idx = M.topk(l, k)
+    counts, offsets, perm, inv = M.schedule(idx.reshape(-1), E)
+    toks = cover_tokens(offsets, perm, inv, k, 100, seed=0)
+    assert len(toks) >= 100 and len(set(toks.tolist())) == len(toks)
+    rows = set(inv.reshape(-1, k)[toks].reshape(-1).tolist())
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            assert a in rows and b - 1 in rows
+        for bm in TILE_HEIGHTS:
+            for r0 in range(a, b, bm):
+                assert any(r in rows for r in range(r0, min(b, r0 + bm))), (e, bm, r0)
