@@ -17,8 +17,9 @@
  *   - Notation: T source tokens, hidden h, expert width m, E router experts, top-k k, E_loc
  *     experts held by this GPU, R = T*k routed rows, assignment a = t*k + j (token t, slot j).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call only enqueues
- *     work on it: no host synchronisation, no allocation, no state kept between calls. Shapes
- *     alone size every launch; the device-side expert counts are never read by the host.
+ *     work on it: no host synchronisation, no allocation, no state kept between calls (the one
+ *     exception, moe_permute_static, keeps a static scratch array per GPU). Shapes alone size
+ *     every launch; the device-side expert counts are never read by the host.
  *   - Ownership: the caller owns every buffer, including workspaces (sized by the *_bytes
  *     queries) and prepared weights. Buffers must not overlap unless stated.
  *   - Alignment: every pointer must be 16-byte aligned (torch allocations are 256-byte aligned).
@@ -29,7 +30,8 @@
  *   - Determinism: there are no floating-point atomics and no split reductions; every sum has a
  *     fixed order, so identical inputs give bitwise identical outputs (the page's "bitwise
  *     deterministic" property, TL;DR and Key claims).
- *   - Thread safety: calls on different streams with different buffers may run concurrently.
+ *   - Thread safety: calls on different streams with different buffers may run concurrently,
+ *     except moe_permute_static calls on one GPU, which share that GPU's scratch array.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -41,13 +43,14 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,
   MOE_EUNSUPPORTED = 2,
-  MOE_EHIP = 3
+  MOE_EHIP = 3,
+  MOE_ENOSCRATCH = 4 /* moe_permute_static: the shape needs more than the static scratch */
 } moe_status;
 
 /* Expert GEMM precision. MOE_MXFP8: E4M3 elements with one E8M0 scale per 32 consecutive elements
@@ -135,6 +138,27 @@ size_t moe_permute_workspace_bytes(const moe_shape* s);
 moe_status moe_permute(const moe_shape* s, moe_dtype dt, const int32_t* assign,
                        const uint16_t* x, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, void* rows, uint8_t* row_scales, void* ws, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_permute_static: moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The same arguments and
+ * results as moe_permute, minus `ws`: the schedule's scratch (moe_permute_workspace_bytes() bytes:
+ * the per-chunk expert histograms, every byte written before it is read, so nothing needs
+ * clearing) is a static device array of MOE_PERMUTE_STATIC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends. Its address on the current device is
+ * looked up once per device on the first call there. The call allocates nothing.
+ * Errors: as moe_permute; MOE_ENOSCRATCH (nothing enqueued) when moe_permute_workspace_bytes()
+ * exceeds MOE_PERMUTE_STATIC_SCRATCH_BYTES (e.g. R * E_loc > 2^31 at 256 assignments per chunk);
+ * MOE_EHIP when the array's address cannot be obtained.
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls that overlap in time on
+ * one GPU (different streams, or threads) race and must be serialised by the caller; calls on
+ * one stream never overlap.
+ * ------------------------------------------------------------------------------------------- */
+#define MOE_PERMUTE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status moe_permute_static(const moe_shape* s, moe_dtype dt, const int32_t* assign,
+                              const uint16_t* x, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* inv, void* rows, uint8_t* row_scales,
+                              void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * moe_expert_ffn: the SwiGLU experts as grouped GEMMs (Key claims: expert grouped GEMMs, MXFP8,

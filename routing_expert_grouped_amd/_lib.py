@@ -11,7 +11,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSCRATCH = 0, 1, 2, 3, 4
+MOE_PERMUTE_STATIC_SCRATCH_BYTES = 8 << 20
 MOE_BF16, MOE_MXFP8 = 0, 1
 
 # every function the header declares, for the symbol check
@@ -19,7 +20,7 @@ EXPORTS = [
     "moe_status_string", "moe_abi_version",
     "moe_prepared_weight_bytes", "moe_prepare_weights",
     "moe_route_workspace_bytes", "moe_route",
-    "moe_permute_workspace_bytes", "moe_permute",
+    "moe_permute_workspace_bytes", "moe_permute", "moe_permute_static",
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
     "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
@@ -76,6 +77,7 @@ def load() -> ctypes.CDLL:
         "moe_route": (I, [S, P, P, P, P, P, P, P, P]),
         "moe_permute_workspace_bytes": (Z, [S]),
         "moe_permute": (I, [S, I, P, P, P, P, P, P, P, P, P, P]),
+        "moe_permute_static": (I, [S, I, P, P, P, P, P, P, P, P, P]),
         "moe_expert_ffn_workspace_bytes": (Z, [S, I]),
         "moe_expert_ffn": (I, [S, I, P, P, P, P, P, P, P]),
         "moe_combine": (I, [S, P, P, P, P, P, P]),

@@ -1,6 +1,7 @@
 // C-ABI front end: argument checks, workspace layout and the launch sequence of each entry point.
 // Nothing here allocates or synchronises; every call only enqueues kernels on the caller's stream.
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -185,6 +186,8 @@ const char* moe_status_string(moe_status s) {
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape not covered by the kernels";
     case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+    case MOE_ENOSCRATCH:
+      return "MOE_ENOSCRATCH: the shape needs more scratch than the static buffer holds";
   }
   return "unknown moe_status";
 }
@@ -250,6 +253,53 @@ moe_status moe_permute(const moe_shape* s, moe_dtype dt, const int32_t* assign,
   else
     e = launch_gather_bf16(x, inv, reinterpret_cast<uint16_t*>(rows), s->T, s->h, s->k, hs);
   return hip_status(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The schedule's scratch for moe_permute_static: one static array per GPU (each device holds its
+// own copy of a __device__ variable). Host code never passes the array's name to a kernel (on the
+// host it only stands in for the symbol): its device address is obtained with hipGetSymbolAddress
+// once per device, with that device current, and kept here.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[MOE_PERMUTE_STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's array, or nullptr on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute_static(const moe_shape* s, moe_dtype dt, const int32_t* assign,
+                              const uint16_t* x, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* inv, void* rows, uint8_t* row_scales,
+                              void* stream) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(assign) || !ok_ptr(x) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(perm) ||
+      !ok_ptr(inv) || !ok_ptr(rows))
+    return MOE_EINVAL;
+  if (dt == MOE_MXFP8 && !ok_ptr(row_scales)) return MOE_EINVAL;
+  if (sched_workspace_bytes(s->T * s->k, s->E_loc) > MOE_PERMUTE_STATIC_SCRATCH_BYTES)
+    return MOE_ENOSCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_EHIP;
+  return moe_permute(s, dt, assign, x, counts, offsets, perm, inv, rows, row_scales, ws, stream);
 }
 
 size_t moe_expert_ffn_workspace_bytes(const moe_shape* s, moe_dtype dt) {
