@@ -32,6 +32,7 @@
 // workgroups find an empty entry and exit, so the host never reads the counts.
 #include <type_traits>
 
+#include "moe_gemm_plan.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -452,46 +453,36 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// K bytes per stage (whole 128-byte lines) and ring depths per tile height. LDS per workgroup:
-// (NS * 256 + NSR * BM) * 128 bytes, at most 160 KB: BM = 256 and 192 take a two-deep weight ring
-// and a three-deep row ring (160 KB, 136 KB), BM = 128 three and four (160 KB). The routed-row
-// ring is one stage deeper: those panels miss L2 more (every XCD streams all of a band's row
-// panels but only its own weight panels).
+// K bytes per stage (whole 128-byte lines). The ring depths per tile height (big_ns, big_nsr) and
+// the DMA issue order and wait counts are in moe_gemm_plan.h. LDS per workgroup:
+// (NS * 256 + NSR * BM) * 128 bytes, at most 160 KB.
 constexpr int kBigRB = 128;
-__host__ __device__ constexpr int big_ns(int bm) { return bm >= 192 ? 2 : 3; }
-__host__ __device__ constexpr int big_nsr(int bm) { return big_ns(bm) + 1; }
 
 template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   constexpr int BN = kBigBN;
-  constexpr int ROWS = BN + BM;
   constexpr int WSTAGE = BN * RB;                // one stage of the weight operand
   constexpr int RSTAGE = BM * RB;                // one stage of the routed rows
   constexpr int NI = 4;                          // weight fragments per wave
   constexpr int NJ = BM / 64;                    // row fragments per wave
-  constexpr int LOADS = ROWS * RB / 16 / 256;    // 16-byte DMA loads per thread per stage
-  constexpr int SLOTS = RB / 16;
-  constexpr int QW = BN * SLOTS / 256;           // of which weight rows
-  constexpr int QR = LOADS - QW;                 // and routed rows
-  constexpr int SPS = MX ? RB / 64 : RB / 32;    // MFMA k-steps per stage
-  constexpr int PC = MX ? 4 / SPS : 1;           // stages per 256-element MX chunk
-  constexpr int NSC = MX ? NI + NJ : 0;          // scale loads per chunk
-  // a barrier point's loads go out in SPS parts, one per k-step of the next stage (the last part
-  // after the following barrier), so the DMA load is spread over the stage. The last part starts
-  // at unit U0, after every weight unit when the weight ring is two deep (its group is needed at
-  // the following barrier), and holds WL weight and RL routed-row units; the other parts split
-  // [0, U0) evenly.
-  constexpr int U0a = (SPS - 1) * (LOADS / SPS);
-  constexpr int U0 = NS == 2 && QW > U0a ? QW : U0a;
-  constexpr int WL = QW > U0 ? QW - U0 : 0;
-  constexpr int RL = LOADS - (U0 > QW ? U0 : QW);
-  // loads a wave has in flight after the later of its two groups of a stage (see wait_stage),
-  // in the steady state
-  constexpr int NFULL = NSR > NS ? QR * (NS - 1) + QW * (NS - 2) : LOADS * (NS - 2);
-  constexpr int NSTEADY = NFULL - WL - RL;
-  static_assert(SPS >= 2 && NSTEADY >= 0 && (NS > 2 || WL == 0), "DMA parts per k-step");
-  static_assert(NSR == NS || NSR == NS + 1, "row ring as deep as the weight ring or one deeper");
-  static_assert(NFULL < 64 && NS >= 2 && NS <= 5, "vmcnt range");
+  // the DMA plan (moe_gemm_plan.h): LOADS 16-byte units per thread per barrier point, QW of the
+  // weight group and QR of the row group (the shallower ring's group first), issued in SPS parts
+  // (one per k-step of the next stage, the last part, units [U0, LOADS), after the following
+  // barrier), and the number of loads each barrier point's wait may leave in flight
+  using PO = BigPlanOf<MX, BM, RB, NS, NSR>;
+  constexpr BigPlan PL = PO::get();
+  constexpr int LOADS = PL.LOADS;
+  constexpr int SLOTS = PL.SLOTS;
+  constexpr int SPS = PL.SPS;                    // MFMA k-steps per stage
+  constexpr int PC = PL.PC;                      // stages per 256-element MX chunk
+  constexpr int NSC = PL.NSC;                    // scale loads per chunk
+  constexpr int NSTEADY = plan_steady_count(PO::get()); // in flight at a steady-state wait
+  constexpr int NDEEP = NS > NSR ? NS : NSR;
+  constexpr int NMAX = LOADS * NDEEP;            // bound of any wait count
+  static_assert(PL.BN == BN && NSC == (MX ? NI + NJ : 0), "plan matches the tile");
+  static_assert(SPS >= 2 && NSTEADY >= 0, "DMA parts per k-step");
+  static_assert(NS >= 2 && NSR >= 2 && NSR >= NS - 1 && NSR <= NS + 1, "ring depths");
+  static_assert(NMAX + NSC < 64, "vmcnt range");
   static_assert(!MX || PC == 2, "an MX chunk of 256 elements is two stages");
   static_assert(MX || SPS % 2 == 0, "fragment double buffer alternates within a stage");
   static_assert(NS * WSTAGE + NSR * RSTAGE <= 160 * 1024, "LDS budget");
@@ -573,20 +564,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 
   // ---- DMA sources: unit id = q * 256 + tid is LDS row id / SLOTS (rows BN.. are the routed
   //      rows, at row id / SLOTS - BN of their ring slot), physical slot id % SLOTS, and must carry
-  //      logical chunk slot ^ f(row) (f(BN + r) = f(r) for BN = 256). Units q < QW are weight
-  //      rows, the rest routed rows; 32-bit offsets from the two (uniform) bases.
+  //      logical chunk slot ^ f(row) (f(BN + r) = f(r) for BN = 256). Unit q of a point is unit
+  //      plan_group_index(q) of the weight group (plan_is_w) or of the row group; 32-bit offsets
+  //      from the two (uniform) bases.
   uint32_t src[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
-    const int id = q * 256 + tid;
-    const int row = id / SLOTS;
-    const int c = (id % SLOTS) ^ big_swz<RB>(row);
-    const uint32_t cb = 16 * c;
-    if (q < QW) {
+    const int u = plan_group_index(PO::get(), q);
+    const int id = u * 256 + tid;
+    const int row = id / SLOTS;  // row of the weight panel, or of the routed-row tile
+    if (plan_is_w(PO::get(), q)) {
+      const uint32_t cb = 16 * ((id % SLOTS) ^ big_swz<RB>(row));
       src[q] = p.w_tiled ? (uint32_t)((size_t)(n0 / BN) * ldk * BN) + row * RB + cb
                          : (uint32_t)((n0 + row) * ldk) + cb;
     } else {
-      int r = row0 + row - BN;
+      const uint32_t cb = 16 * ((id % SLOTS) ^ big_swz<RB>(BN + row));
+      int r = row0 + row;
       r = r < row_end ? r : row_end - 1;  // rows past the expert's end are never stored
       if (p.row_src) r = p.row_src[r] / p.row_div;
       src[q] = (uint32_t)(r * ldk) + cb;
@@ -598,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   const int nk = (int)(ldk / RB);
   const int nchunks = MX ? nk / PC : 0;
   // first unit of part t (t = SPS: the end)
-  auto part_start = [](int t) { return t >= SPS ? LOADS : t * U0 / (SPS - 1); };
+  auto part_start = [](int t) { return plan_part_start(PO::get(), t); };
   // part `part` of barrier point b's groups W(b+NS-1), R(b+NSR-1), skipping stages that do not
   // exist; they go to the ring slots of stage b-1
   auto issue_part = [&](int b, int part) {
@@ -611,10 +604,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
       if (q < q0 || q >= q1) continue;
-      if (q < QW) {
-        if (hw) dma16(wexp + (src[q] + offw), bw + q * 4096);
+      if (plan_is_w(PO::get(), q)) {
+        if (hw) dma16(wexp + (src[q] + offw), bw + plan_group_index(PO::get(), q) * 4096);
       } else {
-        if (hr) dma16(rows_b + (src[q] + offr), br + (q - QW) * 4096);
+        if (hr) dma16(rows_b + (src[q] + offr), br + plan_group_index(PO::get(), q) * 4096);
       }
     }
   };
@@ -667,42 +660,29 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     for (int q = 0; q < NJ; ++q) scr[q] = scale_word(nscr[q]);
   };
 
-  // ---- issue order of this wave's vector-memory loads (fixed, so the counts below are exact).
-  //   Barrier point b's groups are W(b+NS-1) then R(b+NSR-1) (those that exist), as units
-  //   0 .. LOADS-1, weight units first. The prologue issues S(0) and all groups of the points
-  //   b = -(NSR-1) .. -1. Stage j then issues part t of point j's groups in its k-step t, the
-  //   last part right after barrier point j+1, followed by S(cc+1) when j+1 = cc * PC + 1 and
-  //   chunk cc+1 exists.
-  //   Loads complete in issue order, so point j, which needs W(j) and R(j), waits until only the
-  //   loads issued after the later of the two are left. With every group of the points before j
-  //   issued, those would be:
-  //     NSR == NS + 1: W(j) is later; after it come R(j+1 .. j+NS-1) and W(j+1 .. j+NS-2);
-  //     NSR == NS:     R(j) is later; after it come W and R of j+1 .. j+NS-2;
-  //   each only if that stage exists (< nk); the last part of point j-1 is not issued yet, so
-  //   its units are taken off. Scale loads issued after them are not counted, which only makes
-  //   the wait stricter (they complete too), never too weak.
-  auto last_part = [&](int b) {
-    return (b + NS - 1 >= 0 && b + NS - 1 < nk ? WL : 0) +
-           (b + NSR - 1 >= 0 && b + NSR - 1 < nk ? RL : 0);
-  };
+  // ---- issue order of this wave's vector-memory loads (fixed, so the counts are exact): the
+  //   prologue issues S(0) and every point b < 0 whole; stage j then issues part t of point j's
+  //   groups in its k-step t, the last part right after barrier point j+1, preceded by S(cc+1)
+  //   when j+1 = cc * PC + 1 and chunk cc+1 exists (the branch-free k-steps issue S(cc+1) at the
+  //   start of stage cc * PC instead). Loads complete in issue order, so point j waits until at
+  //   most plan_wait_count(j) loads are in flight: the DMA units issued after the later of W(j),
+  //   R(j). Scale loads issued after them are not counted, which only makes the wait stricter.
   auto wait_stage = [&](int j) {
-    const int nw = max(0, min(j + NS - 2, nk - 1) - j);  // stages j+1 .. j+NS-2 that exist
-    int n;
-    if constexpr (NSR > NS) n = QR * max(0, min(j + NS - 1, nk - 1) - j) + QW * nw;
-    else n = LOADS * nw;
-    if (j >= 1) n -= last_part(j - 1);
+    const int n = plan_wait_count(PO::get(), j, nk);
     asm volatile("" ::: "memory");
-    wait_vmcnt_range<0, NFULL>(n);
+    wait_vmcnt_range<0, NMAX>(n);
   };
   // barrier point j: stage j is in LDS for every wave and stage j-1 read by every wave; then the
   // last part of point j-1's loads and the scale words of the next chunk
+  // (the scale words go out before the last part: the DMA units issued after them are then all
+  // counted by the wait of the next chunk's first point, which therefore covers them)
   auto barrier_point = [&](int j) {
     wait_stage(j);
     lds_barrier();
-    if (j >= 1) issue_part(j - 1, SPS - 1);
     if constexpr (MX) {
       if (j % PC == 1 && j / PC + 1 < nchunks) sload(j / PC + 1, nscw, nscr);
     }
+    if (j >= 1) issue_part(j - 1, SPS - 1);
   };
 
   // ---- fragment byte offsets inside a stage: row * RB + 16 * (c ^ f(row)) == fb ^ (16 c)
@@ -777,7 +757,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     sload(0, nscw, nscr);
   }
 #pragma unroll
-  for (int b = -(NSR - 1); b < 0; ++b)
+  for (int b = -(NDEEP - 1); b < 0; ++b)
 #pragma unroll
     for (int part = 0; part < SPS; ++part) issue_part(b, part);
   barrier_point(0);
@@ -789,7 +769,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
 
-  // ---- steady-state k-step (stage j with j + NSR < nk, so every wait and load is unconditional):
+  // ---- steady-state k-step (stage j with j + max(NS, NSR) < nk, so every wait and load is
+  // unconditional):
   // its MFMAs interleaved one by one with the other work, in a fixed order the compiler may not
   // change (sched_barrier): part t of barrier point j's DMA (into stage j-1's ring slots), the
   // next k-step's LDS reads, and in a stage's last k-step, right after the first MFMA, the wait
@@ -800,14 +781,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     constexpr int P = decltype(p_tag)::value;
     constexpr bool LAST = t + 1 == SPS;
     constexpr bool SCALES = MX && t == 0 && P == 0;  // the first k-step of chunk cc
-    constexpr int Q0 = t * U0 / (SPS - 1);  // this k-step's DMA part: units [Q0, Q0 + NDMA)
-    constexpr int NDMA = (t + 1 == SPS ? LOADS : (t + 1) * U0 / (SPS - 1)) - Q0;
+    constexpr int Q0 = plan_part_start(PO::get(), t);  // this k-step's DMA part: units [Q0, Q0 + NDMA)
+    constexpr int NDMA = plan_part_start(PO::get(), t + 1) - Q0;
     constexpr int NSCL = SCALES ? NSC : 0;
     // the scale words of chunk cc + 1 went out at the start of stage cc * PC = j - P, as the
-    // first loads of that stage; they follow every load of stage j + 1's later group, and so
-    // are in flight beside the NSTEADY loads at point j + 1, when that group's last part went
-    // out at a barrier point up to j - P (which is j + 3 - NS at the latest)
-    constexpr int SCL_AFTER = MX && P <= NS - 3 ? NSC : 0;
+    // first loads of that stage; they may still be in flight at the wait of point j + 1 when both
+    // of stage j + 1's groups went out before them (plan_scales_in_flight)
+    constexpr int SCL_AFTER = plan_scales_in_flight(PO::get(), P);
     constexpr int NOPS = NDMA + NSCL + NR;
     constexpr int SLOTS_M = NM - 2;  // leave the last two MFMAs to cover the last reads
     constexpr int K = (NOPS + SLOTS_M - 1) / SLOTS_M;
@@ -841,8 +821,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
             }
           } else if (op < NSCL + NDMA) {
             const int q = Q0 + op - NSCL;
-            if (q < QW) dma16(wexp + (src[q] + doffw), dbw + q * 4096);
-            else dma16(rows_b + (src[q] + doffr), dbr + (q - QW) * 4096);
+            const int u = plan_group_index(PO::get(), q);
+            if (plan_is_w(PO::get(), q)) dma16(wexp + (src[q] + doffw), dbw + u * 4096);
+            else dma16(rows_b + (src[q] + doffr), dbr + u * 4096);
           } else {
             load_piece(nxt, rbw, rbr, rt, op - NDMA - NSCL);
           }
@@ -910,8 +891,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
       for (int j = j0; j < j1; ++j) stage(j, I0{}, fast_tag, FA, FB);
     }
   };
-  // steady state: stages j with j + NSR < nk (rounded down to whole MX chunks), then the rest
-  const int jsteady = max(0, (nk - NSR) / PC * PC);
+  // steady state: stages j with j + max(NS, NSR) < nk (rounded down to whole MX chunks), then
+  // the rest
+  const int jsteady = plan_steady_end(PO::get(), nk);
   run(0, jsteady, std::true_type{});
   run(jsteady, nk, std::false_type{});
   }  // nk > 0
@@ -1350,8 +1332,8 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
 // kernels launched by name in non-template functions, so that each instantiation is compiled for
 // the device
 #define MOE_BIG(MODEV, MXV, BMV, G, A)                                                          \
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV, kBigRB, big_ns(BMV),             \
-                                              big_nsr(BMV)>),                                   \
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV, kBigRB, big_ns(MXV, BMV),        \
+                                              big_nsr(MXV, BMV)>),                              \
                      G, dim3(256), 0, st, A)
 
 // grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most

@@ -1,0 +1,221 @@
+"""The large-tile grouped GEMM's DMA pipeline, checked on the host: for every tile configuration the
+launchers instantiate (and every ring-depth pair the plan allows), and every K length of 1..200
+stages, a replay of the kernel's issue order shows that each barrier point's wait, with the count
+the kernel uses (plan_wait_count / plan_steady_count in moe_gemm_plan.h, compiled here with g++),
+leaves none of the stage's loads in flight, that the MX scale words a chunk reads have arrived,
+that no ring slot is overwritten before the stage in it has been read, and that every count fits
+the vmcnt field.
+
+The replay models the kernel's program order (grouped_gemm_big_kernel): the prologue issues the
+first chunk's scale words (MX) and every barrier point b < 0 whole; stage j issues part t of point
+j's groups in k-step t and its last part right after the barrier of point j + 1; the branch-free
+k-steps (stages below plan_steady_end) issue the next chunk's scale words at the start of a
+chunk's first stage and wait with the steady count, the others issue them right after barrier
+point cc * PC + 1 (before that point's last part) and wait with plan_wait_count. Vector-memory
+loads complete in issue order, so a wait for "at most n in flight" completes everything but the
+last n loads issued. The GPU is not used."""
+import json
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "routing_expert_grouped_amd", "csrc")
+HEADER = os.path.join(CSRC, "moe_gemm_plan.h")
+KERNELS = os.path.join(CSRC, "moe_gemm_kernels.hip")
+NK_MAX = 200
+
+PROGRAM = r"""
+#include <cstdio>
+#include "moe_gemm_plan.h"
+using namespace moe;
+static void dump(bool mx, int bm, int ns, int nsr, bool inst) {
+  const BigPlan p = make_big_plan(mx, bm, 128, ns, nsr);
+  std::printf("{\"mx\": %d, \"bm\": %d, \"ns\": %d, \"nsr\": %d, \"inst\": %d, \"loads\": %d, "
+              "\"qw\": %d, \"qr\": %d, \"sps\": %d, \"pc\": %d, \"nsc\": %d, \"rfirst\": %d, "
+              "\"u0\": %d, \"steady\": %d, \"scl\": [%d, %d], \"parts\": [",
+              mx, bm, ns, nsr, inst, p.LOADS, p.QW, p.QR, p.SPS, p.PC, p.NSC, p.RFIRST, p.U0,
+              plan_steady_count(p), plan_scales_in_flight(p, 0), plan_scales_in_flight(p, 1));
+  for (int t = 0; t <= p.SPS; ++t) std::printf("%s%d", t ? ", " : "", plan_part_start(p, t));
+  std::printf("], \"w\": [");
+  for (int q = 0; q < p.LOADS; ++q) std::printf("%s%d", q ? ", " : "", plan_is_w(p, q));
+  std::printf("], \"counts\": {");
+  for (int nk = 1; nk <= %NK%; ++nk) {
+    std::printf("%s\"%d\": [%d", nk > 1 ? ", " : "", nk, plan_steady_end(p, nk));
+    for (int j = 0; j < nk; ++j) std::printf(", %d", plan_wait_count(p, j, nk));
+    std::printf("]");
+  }
+  std::printf("}}\n");
+}
+#define INST(MX, BM) dump(MX, BM, big_ns(MX, BM), big_nsr(MX, BM), true);
+int main() {
+  MOE_BIG_TILE_CONFIGS(INST)
+  // every other ring-depth pair the plan supports within the LDS budget
+  const bool mxs[2] = {true, false};
+  const int bms[3] = {128, 192, 256};
+  for (bool mx : mxs)
+    for (int bm : bms)
+      for (int ns = 2; ns <= 5; ++ns)
+        for (int nsr = ns - 1; nsr <= ns + 1; ++nsr) {
+          if (nsr < 2 || (ns * 256 + nsr * bm) * 128 > 160 * 1024) continue;
+          if (mx && bm == 256) continue;  // does not fit the register file
+          dump(mx, bm, ns, nsr, false);
+        }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def plans():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "plan.cpp")
+        exe = os.path.join(d, "plan")
+        open(src, "w").write(PROGRAM.replace("%NK%", str(NK_MAX)))
+        subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", CSRC, src, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return [json.loads(line) for line in out.splitlines()]
+
+
+def replay(p, nk):
+    """Issue order of one wave over a K loop of nk stages; raises AssertionError on a violation."""
+    ns, nsr, loads, sps, pc, nsc = p["ns"], p["nsr"], p["loads"], p["sps"], p["pc"], p["nsc"]
+    mx = bool(p["mx"])
+    parts = p["parts"]
+    is_w = p["w"]
+    counts = p["counts"][str(nk)]
+    jsteady, waits = counts[0], counts[1:]
+    nchunks = nk // pc if mx else 0
+    seq = []          # issued loads: ("W", stage) / ("R", stage) / ("S", chunk)
+    last = {}         # (kind, stage) -> index in seq of its last load, and how many were issued
+    issued = {}
+    barriers = [0]    # the last barrier point passed
+    done_upto = [0]   # loads seq[:done_upto] are complete (in-order completion)
+    scales = {"pending": None}
+
+    def exists(s):
+        return 0 <= s < nk
+
+    def dma(kind, s):
+        depth = ns if kind == "W" else nsr
+        prev = s - depth  # the stage that last used this ring slot
+        if prev >= 0:
+            assert barriers[0] >= prev + 1, f"{kind}({s}) overwrites stage {prev} before it is read"
+        last[(kind, s)] = len(seq)
+        issued[(kind, s)] = issued.get((kind, s), 0) + 1
+        seq.append((kind, s))
+
+    def issue_part(b, t):
+        for q in range(parts[t], parts[t + 1]):
+            kind = "W" if is_w[q] else "R"
+            s = b + (ns if kind == "W" else nsr) - 1
+            if exists(s):
+                dma(kind, s)
+
+    def sload(cc):
+        for _ in range(nsc):
+            seq.append(("S", cc))
+        scales["pending"] = (len(seq) - nsc, len(seq))
+
+    def wait(j, n):
+        assert 0 <= n and n + (nsc if mx else 0) < 64, (j, n)
+        complete = len(seq) - n
+        assert complete >= 0
+        done_upto[0] = max(done_upto[0], complete)
+        got = issued.get(("W", j), 0) + issued.get(("R", j), 0)
+        expect = p["qw"] + p["qr"]  # every unit of both groups, issued before the wait
+        assert got == expect, f"stage {j}: {got} of {expect} loads issued by its wait"
+        assert max(last[("W", j)], last[("R", j)]) < done_upto[0], \
+            f"stage {j} still in flight at its wait (n = {n})"
+        barriers[0] = j
+
+    def take_scales():
+        a, b = scales["pending"]
+        assert b <= done_upto[0], "scale words read before they arrived"
+
+    if mx:
+        sload(0)
+    for b in range(-(max(ns, nsr) - 1), 0):
+        for t in range(sps):
+            issue_part(b, t)
+    wait(0, waits[0])
+    if mx:
+        take_scales()
+    for j in range(nk):
+        P = j % pc
+        fast = j < jsteady
+        if fast:
+            assert j + max(ns, nsr) < nk
+        for t in range(sps):
+            if t < sps - 1:
+                if fast and mx and t == 0 and P == 0:
+                    sload(min(j // pc + 1, nchunks - 1))
+                issue_part(j, t)
+            else:
+                if fast:
+                    if mx and t == 0 and P == 0:
+                        sload(min(j // pc + 1, nchunks - 1))
+                    steady = p["steady"] + p["scl"][P]
+                    assert waits[j + 1] == p["steady"], (j, waits[j + 1], p["steady"])
+                    wait(j + 1, steady)
+                    issue_part(j, sps - 1)
+                elif j + 1 < nk:
+                    wait(j + 1, waits[j + 1])
+                    if mx and (j + 1) % pc == 1 and (j + 1) // pc + 1 < nchunks:
+                        sload((j + 1) // pc + 1)
+                    issue_part(j, sps - 1)
+        if mx and P == pc - 1 and j + 1 < nk:
+            take_scales()
+    # every load of every stage was issued exactly once
+    for s in range(nk):
+        assert issued.get(("W", s)) == p["qw"] and issued.get(("R", s)) == p["qr"], s
+
+
+def test_plan_covers_every_instantiation(plans):
+    """Every (MXFP8, tile height) the launchers instantiate is in MOE_BIG_TILE_CONFIGS."""
+    text = open(KERNELS).read()
+    consts = dict(re.findall(r"constexpr int (k\w+) = (\d+);", text))
+    used = set()
+    for mx, bm in re.findall(r"MOE_BIG\(\s*\w+\s*,\s*(true|false)\s*,\s*(\w+)\s*,", text):
+        used.add((mx == "true", int(consts.get(bm, bm))))
+    listed = {(bool(p["mx"]), p["bm"]) for p in plans if p["inst"]}
+    assert used and used <= listed, used - listed
+
+
+@pytest.mark.parametrize("which", ["instantiated", "other depths"])
+def test_waits_cover_every_stage(plans, which):
+    sel = [p for p in plans if bool(p["inst"]) == (which == "instantiated")]
+    assert sel
+    for p in sel:
+        for nk in range(1, NK_MAX + 1):
+            if p["mx"] and nk % p["pc"]:
+                continue  # an MX row is whole 256-element chunks
+            try:
+                replay(p, nk)
+            except AssertionError as e:
+                raise AssertionError(f"mx={p['mx']} bm={p['bm']} ns={p['ns']} nsr={p['nsr']} "
+                                     f"nk={nk}: {e}") from None
+
+
+def test_replay_catches_a_wrong_count(plans):
+    """The replay is not vacuous: one count made one too small (a wait that leaves a stage's
+    last load in flight) or a scale-word allowance on a chunk's first wait is reported."""
+    p = dict(next(q for q in plans if q["inst"] and q["mx"]))
+    nk = 40
+    counts = {k: list(v) for k, v in p["counts"].items()}
+    bad = list(counts[str(nk)])
+    j = 5
+    bad[1 + j] += 1  # one more load allowed in flight at point j than the plan says
+    p2 = dict(p, counts=dict(counts, **{str(nk): bad}))
+    with pytest.raises(AssertionError):
+        for _ in [0]:
+            # the steady count must match too, so drop to the generic path for this check
+            p2["counts"][str(nk)][0] = 0
+            replay(p2, nk)
+    p3 = dict(p, scl=[p["nsc"] + 1, p["nsc"] + 1])
+    with pytest.raises(AssertionError):
+        replay(p3, nk)
