@@ -662,11 +662,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
 
   // ---- issue order of this wave's vector-memory loads (fixed, so the counts are exact): the
   //   prologue issues S(0) and every point b < 0 whole; stage j then issues part t of point j's
-  //   groups in its k-step t, the last part right after barrier point j+1, preceded by S(cc+1)
-  //   when j+1 = cc * PC + 1 and chunk cc+1 exists (the branch-free k-steps issue S(cc+1) at the
-  //   start of stage cc * PC instead). Loads complete in issue order, so point j waits until at
-  //   most plan_wait_count(j) loads are in flight: the DMA units issued after the later of W(j),
-  //   R(j). Scale loads issued after them are not counted, which only makes the wait stricter.
+  //   groups in its k-step t and the last part right after barrier point j+1; a chunk's first
+  //   stage cc * PC starts with S(cc+1), the next chunk's scale words, ahead of its DMA parts
+  //   (so the wait of chunk cc+1's first point covers them). Loads complete in issue order, so
+  //   point j waits until at most plan_wait_count(j) loads are in flight: the DMA units issued
+  //   after the later of W(j), R(j).
   auto wait_stage = [&](int j) {
     const int n = plan_wait_count(PO::get(), j, nk);
     asm volatile("" ::: "memory");
@@ -674,14 +674,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   };
   // barrier point j: stage j is in LDS for every wave and stage j-1 read by every wave; then the
   // last part of point j-1's loads and the scale words of the next chunk
-  // (the scale words go out before the last part: the DMA units issued after them are then all
-  // counted by the wait of the next chunk's first point, which therefore covers them)
   auto barrier_point = [&](int j) {
     wait_stage(j);
     lds_barrier();
-    if constexpr (MX) {
-      if (j % PC == 1 && j / PC + 1 < nchunks) sload(j / PC + 1, nscw, nscr);
-    }
     if (j >= 1) issue_part(j - 1, SPS - 1);
   };
 
@@ -838,6 +833,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
     constexpr int t = decltype(t_tag)::value;
     constexpr int P = decltype(p_tag)::value;
     if constexpr (t + 1 < SPS) {
+      if constexpr (MX && t == 0 && P == 0) {  // a chunk's first k-step: the next chunk's scales
+        if (j / PC + 1 < nchunks) sload(j / PC + 1, nscw, nscr);
+      }
       issue_part(j, t);
       load_frags(nxt, j, t + 1);
     } else {

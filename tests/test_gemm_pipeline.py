@@ -9,9 +9,9 @@ the vmcnt field.
 The replay models the kernel's program order (grouped_gemm_big_kernel): the prologue issues the
 first chunk's scale words (MX) and every barrier point b < 0 whole; stage j issues part t of point
 j's groups in k-step t and its last part right after the barrier of point j + 1; the branch-free
-k-steps (stages below plan_steady_end) issue the next chunk's scale words at the start of a
-chunk's first stage and wait with the steady count, the others issue them right after barrier
-point cc * PC + 1 (before that point's last part) and wait with plan_wait_count. Vector-memory
+k-steps (stages below plan_steady_end) wait with the steady count, the others with
+plan_wait_count; both issue the next chunk's scale words at the start of a chunk's first stage,
+ahead of its DMA part. Vector-memory
 loads complete in issue order, so a wait for "at most n in flight" completes everything but the
 last n loads issued. The GPU is not used."""
 import json
@@ -152,8 +152,11 @@ def replay(p, nk):
             assert j + max(ns, nsr) < nk
         for t in range(sps):
             if t < sps - 1:
-                if fast and mx and t == 0 and P == 0:
-                    sload(min(j // pc + 1, nchunks - 1))
+                if mx and t == 0 and P == 0:
+                    if fast:
+                        sload(min(j // pc + 1, nchunks - 1))
+                    elif j // pc + 1 < nchunks:
+                        sload(j // pc + 1)
                 issue_part(j, t)
             else:
                 if fast:
@@ -165,8 +168,6 @@ def replay(p, nk):
                     issue_part(j, sps - 1)
                 elif j + 1 < nk:
                     wait(j + 1, waits[j + 1])
-                    if mx and (j + 1) % pc == 1 and (j + 1) // pc + 1 < nchunks:
-                        sload((j + 1) // pc + 1)
                     issue_part(j, sps - 1)
         if mx and P == pc - 1 and j + 1 < nk:
             take_scales()
