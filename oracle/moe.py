@@ -430,3 +430,65 @@ def expert_weight_grads(wl, inp: dict, assign: np.ndarray, assign_w: np.ndarray,
     wg, wu, wd = (bf16_to_f64(v) for v in weights_of(e))
     _, dwg, dwu, dwd = expert_backward(a, dO, wg, wu, wd, mx=mx)
     return dwg, dwu, dwd
+
+
+# ----------------------------------------------------------------------------------------------
+# Backward through the gate weights and the router
+# ----------------------------------------------------------------------------------------------
+
+
+def gate_grads(dy: np.ndarray, O: np.ndarray, inv: np.ndarray, k: int) -> np.ndarray:
+    """dL/dw[t, j] = <dY[t], O[inv[t*k + j]]>: the combine y[t] = S[t] + sum_j w[t, j] O_row is
+    linear in each gate weight. O are the expert outputs the forward combined. A dropped
+    assignment (inv = -1) has no output row and gets 0. float64, shape [T, k]."""
+    inv = np.asarray(inv, dtype=np.int64).reshape(-1, k)
+    g = np.zeros(inv.shape, dtype=np.float64)
+    for j in range(k):
+        sel = inv[:, j] >= 0
+        g[sel, j] = np.einsum("th,th->t", dy[sel], O[inv[sel, j]])
+    return g
+
+
+def selected_logit_grads(w: np.ndarray, dgate: np.ndarray) -> np.ndarray:
+    """Gradient of the loss with respect to the k selected logits of each token, through the
+    renormalised softmax w_j = exp(l_j) / sum over selected i of exp(l_i):
+      dl_j = w_j * (dgate_j - sum_i w_i dgate_i).
+    The top-k selection itself is piecewise constant in the logits, so the other logits get 0
+    (Reading: the gradient of the selection is taken as zero almost everywhere). [T, k]."""
+    w = np.asarray(w, dtype=np.float64)
+    s = np.sum(w * dgate, axis=1, keepdims=True)
+    return w * (dgate - s)
+
+
+def router_backward(x: np.ndarray, w_router: np.ndarray, idx: np.ndarray, dl: np.ndarray):
+    """The router's own gradients from the selected-logit gradients dl [T, k] of the experts idx
+    [T, k], with logits l[t, e] = sum_i x[t, i] W_r[e, i] + b[e]:
+      dlogits[t, e] = dl[t, j] where idx[t, j] = e, else 0      [T, E]
+      dW_r = dlogits^T x   [E, h];   db = sum_t dlogits[t]   [E];   dX_router = dlogits W_r   [T, h]
+    x, w_router: bf16 bits. float64. Returns (dW_r, db, dX_router, dlogits)."""
+    xf = bf16_to_f64(x)
+    wf = bf16_to_f64(w_router)
+    T, k = idx.shape
+    E = wf.shape[0]
+    dlogits = np.zeros((T, E), dtype=np.float64)
+    for j in range(k):
+        e = np.asarray(idx[:, j], dtype=np.int64)
+        ok = (e >= 0) & (e < E)
+        np.add.at(dlogits, (np.nonzero(ok)[0], e[ok]), dl[ok, j])
+    return dlogits.T @ xf, dlogits.sum(axis=0), dlogits @ wf, dlogits
+
+
+def layer_backward_full(wl, inp: dict, fwd: dict, weights_of, dy_f64=None, mx=None):
+    """The whole layer's backward: the expert path (layer_backward, gate weights fixed) plus the
+    gradients through the gate weights. Returns a dict with dX (expert path + router part for a
+    router layer), dW (per expert), dgate [T, k] and, for a router layer, dW_r, db, dlogits.
+    fwd: layer_forward(..., keep=True) of the same inputs (its O are the expert outputs)."""
+    dy = bf16_to_f64(inp["dy"]) if dy_f64 is None else dy_f64
+    dX, dW = layer_backward(wl, inp, fwd, weights_of, dy_f64=dy, mx=mx)
+    dgate = gate_grads(dy, fwd["O"], fwd["inv"], wl.k)
+    out = {"dX": dX, "dW": dW, "dgate": dgate}
+    if wl.mode == "router":
+        dl = selected_logit_grads(fwd["w"], dgate)
+        dWr, db, dXr, dlogits = router_backward(inp["x"], inp["w_router"], fwd["idx"], dl)
+        out.update(dX=dX + dXr, dW_r=dWr, db=db, dlogits=dlogits, dl=dl)
+    return out
