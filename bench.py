@@ -199,7 +199,9 @@ def cpu_baseline(wl, inp, weights_of, shared_host, n_tokens: int, min_seconds: f
 def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
     """The expert-path backward of the same layer, timed on its own: one forward that keeps its
     saved state (timed too, as the training forward), then K backward steps from that state, each
-    with HIP events at its stage boundaries. Weight gradients in float32."""
+    with HIP events at its stage boundaries. Weight gradients in float32. Then K steps of the whole
+    layer's backward (moe_backward_layer: also the gate-weight, router-matrix and bias gradients
+    and the router's part of dX), timed as a whole."""
     import torch
 
     dev = x.device
@@ -235,6 +237,18 @@ def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
             stages[k] += v / args.steps
     for ev in evs + [wev]:
         ev.close()
+    # the whole layer's backward: the expert path plus the gate-weight and router gradients
+    wr = kw.get("w_router")
+    lay = lambda: G.moe_backward_layer(sh, wl.dtype, x, dy, saved, pbwd, w_router=wr, dx=dx,
+                                       dw=dw, ws=bws)
+    for _ in range(args.warmup):
+        lay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lay()
+    torch.cuda.synchronize()
+    layer_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     R = wl.T * wl.k
     flops = 12.0 * R * wl.h * wl.m  # dH, dA (dgrad) and the three weight gradients
     peak = PEAK_TFLOPS[wl.dtype]
@@ -243,6 +257,7 @@ def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
     return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "gemm_mfma_frac": round(flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
             "flop": flops, "dw_dtype": "f32", "training_forward_ms": round(fwd_saved_ms, 4),
+            "layer_backward_ms": round(layer_ms, 4),
             "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
 
 

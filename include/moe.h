@@ -198,9 +198,11 @@ moe_status moe_combine(const moe_shape* s, const uint16_t* out_rows, const int32
  *   weights given by the caller (one expert-parallel rank's share).
  * prepared: E_loc experts from moe_prepare_weights(dt); shared_prepared: BF16 shared expert
  *   (shape.m_shared > 0) or NULL. y [T][h] bf16 output.
- * saved: NULL, or moe_saved_bytes() bytes that receive what moe_backward needs (training): the
- *   schedule (offsets, perm, inv), the gate weight of every assignment and GEMM-1's G and U in
- *   float32. Needs h % 256 == 0 and m % 256 == 0 (else MOE_EUNSUPPORTED).
+ * saved: NULL, or moe_saved_bytes() bytes that receive what the backward needs (training): the
+ *   schedule (offsets, perm, inv), the gate weight and local expert of every assignment, GEMM-1's
+ *   G and U in float32 and the expert outputs [R][h] bf16 (GEMM-2 writes them there instead of
+ *   into ws, so the out_rows view is then not written). Needs h % 256 == 0 and m % 256 == 0 (else
+ *   MOE_EUNSUPPORTED).
  * ws: moe_forward_workspace_bytes() bytes. The intermediates stay in it; moe_forward_views()
  *   gives their addresses.
  * Gather: when h % 256 == 0 and 2m % 256 == 0 the first grouped GEMM reads routed row r straight
@@ -284,6 +286,28 @@ size_t moe_backward_workspace_bytes(const moe_shape* s, moe_dtype dt);
 moe_status moe_backward(const moe_shape* s, moe_dtype dt, const uint16_t* x, const uint16_t* dy,
                         const void* saved, const void* prepared_bwd, uint16_t* dx, void* dw_gate,
                         void* dw_up, void* dw_down, int dw_fp32, void* ws, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_backward_layer: the whole layer's backward (the page's Key claims measure the backward of
+ * the whole isolated layer): the expert path as moe_backward, plus the gradients through the gate
+ * weights, which moe_backward holds fixed. From the forward's expert outputs O (kept in `saved`):
+ *   dgate[a] = <dY[t], O[inv[a]]>, t = a / k (0 for a dropped assignment)       [T*k] float out
+ * Router use (w_router != NULL, the [E][h] bf16 matrix of the forward; E_loc == E): the gate
+ * weights are the softmax of the k selected logits and the selection carries no gradient, so
+ *   dl[t, j] = w[t, j] (dgate[t, j] - sum_i w[t, i] dgate[t, i]),
+ *   dw_router[e] = sum over expert e's assignments of dl * x[t]   [E][h] float out (required),
+ *   dbias[e] = sum over expert e's assignments of dl               [E] float out or NULL,
+ * and dx also receives sum_j dl[t, j] w_router[e_j] (added before its one rounding, after the
+ * expert path's rows, j ascending). Expert-share use (w_router == NULL): dw_router and dbias must
+ * be NULL; dgate is what the owner of the router needs. Every sum has a fixed order (the router
+ * matrix gradient over each expert's rows in schedule order, in chunks of 64 rows added in order).
+ * ws: moe_backward_workspace_bytes() (for E == E_loc it holds the router's scratch too).
+ * ------------------------------------------------------------------------------------------- */
+moe_status moe_backward_layer(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                              const uint16_t* w_router, const uint16_t* dy, const void* saved,
+                              const void* prepared_bwd, uint16_t* dx, void* dw_gate, void* dw_up,
+                              void* dw_down, int dw_fp32, float* dgate, float* dw_router,
+                              float* dbias, void* ws, void* stream);
 
 /* Profiling variant of moe_backward, events recorded at its stage boundaries:
  *   ev[0] tables ev[1] un-combine ev[2] dH + SwiGLU backward ev[3] dA ev[4] un-permute ev[5]

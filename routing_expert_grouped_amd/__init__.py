@@ -26,7 +26,8 @@ __all__ = [
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
-    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_profiled",
+    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
+    "moe_backward_profiled",
 ]
 
 
@@ -437,6 +438,32 @@ def moe_backward(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, dx=None, dw
                                           dw_fp32, ws, stream)
     check("moe_backward", load().moe_backward(*args, st.cuda_stream))
     return dx, dw, ws
+
+
+def moe_backward_layer(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, w_router=None,
+                       dx=None, dw=None, dw_fp32: bool = True, dgate=None, dw_router=None,
+                       dbias=None, ws=None, stream=None):
+    """The whole layer's backward: the expert path plus the gate-weight gradients dgate [T*k]
+    and, with w_router (router use), the router matrix and bias gradients (its part of dx is
+    included). Returns (dx, (dw_gate, dw_up, dw_down), dgate, dw_router, dbias, ws); dw_router
+    and dbias are None for an expert share."""
+    args, dx, dw, ws, st = _backward_args(shape, dtype, x, dy, saved, prepared_bwd, dx, dw,
+                                          dw_fp32, ws, stream)
+    T, k, E, h = shape.T, shape.k, shape.E, shape.h
+    dev = _dev(x)
+    with torch.cuda.stream(st):
+        dgate = torch.empty(T * k, dtype=torch.float32, device=dev) if dgate is None else dgate
+        if w_router is not None:
+            dw_router = torch.empty(E, h, dtype=torch.float32, device=dev) if dw_router is None \
+                else dw_router
+            dbias = torch.empty(E, dtype=torch.float32, device=dev) if dbias is None else dbias
+    # insert w_router after x, then the gate outputs before ws
+    largs = args[:3] + [_ptr(w_router, "w_router", torch.bfloat16, E * h)] + args[3:11] + [
+        _ptr(dgate, "dgate", torch.float32, T * k),
+        _ptr(dw_router, "dw_router", torch.float32, E * h),
+        _ptr(dbias, "dbias", torch.float32, E)] + args[11:]
+    check("moe_backward_layer", load().moe_backward_layer(*largs, st.cuda_stream))
+    return dx, dw, dgate, dw_router, dbias, ws
 
 
 def moe_backward_profiled(shape: MoeShape, dtype, x, dy, saved, prepared_bwd, events: HipEvents,

@@ -25,7 +25,8 @@ EXPORTS = [
     "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
-    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_profiled",
+    "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
+    "moe_backward_profiled",
 ]
 
 MOE_PROFILE_EVENTS = 10
@@ -90,6 +91,7 @@ def load() -> ctypes.CDLL:
         "moe_prepare_bwd_weights": (I, [S, I, P, P, P, P, P]),
         "moe_backward_workspace_bytes": (Z, [S, I]),
         "moe_backward": (I, [S, I, P, P, P, P, P, P, P, P, I, P, P]),
+        "moe_backward_layer": (I, [S, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P]),
         "moe_backward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, I, P, P, P]),
     }
     for name, (res, args) in sig.items():

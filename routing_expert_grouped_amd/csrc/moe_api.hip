@@ -55,7 +55,7 @@ moe_status check_backward_shape(const moe_shape* s, moe_dtype dt) {
 
 // Saved activations of a training forward (moe_saved_bytes).
 struct SavedLayout {
-  size_t offsets, perm, inv, w, gu, total;
+  size_t offsets, perm, inv, w, assign, gu, o, total;
 };
 
 SavedLayout saved_layout(const moe_shape* s) {
@@ -71,7 +71,9 @@ SavedLayout saved_layout(const moe_shape* s) {
   L.perm = take(R * 4);
   L.inv = take(R * 4);
   L.w = take(R * 4);
-  L.gu = take(R * 2 * s->m * 4);  // float32
+  L.assign = take(R * 4);              // each assignment's local expert
+  L.gu = take(R * 2 * s->m * 4);       // float32
+  L.o = take(R * (size_t)s->h * 2);    // the expert outputs (GEMM-2 writes them here), bf16
   L.total = off;
   return L;
 }
@@ -81,6 +83,10 @@ struct BackwardLayout {
   size_t tiles, koff, dO, dO_s, dgu, dgu_s, dgu_f32, dA, At, At_s, dOt, dOt_s, Ht, Ht_s, dGUt,
       dGUt_s, total;
   int kmax;
+  // the router's gradients (shapes with E == E_loc): selected-logit gradients, the chunk tile
+  // table and the partial sums of the router-matrix gradient
+  size_t dl, rtiles, rpartial, rpartial_db;
+  int rmax_tiles;
 };
 
 BackwardLayout backward_layout(const moe_shape* s, moe_dtype dt) {
@@ -113,6 +119,13 @@ BackwardLayout backward_layout(const moe_shape* s, moe_dtype dt) {
   L.Ht_s = mx ? take(m * km / kMxBlock) : 0;
   L.dGUt = take(2 * m * km * el);
   L.dGUt_s = mx ? take(2 * m * km / kMxBlock) : 0;
+  if (s->E == s->E_loc) {
+    L.rmax_tiles = (int)router_wgrad_tiles(R, s->E_loc);
+    L.dl = take((size_t)R * 4);
+    L.rtiles = take(align_up(sizeof(int)) + (size_t)L.rmax_tiles * sizeof(int2));
+    L.rpartial = take((size_t)L.rmax_tiles * h * 4);
+    L.rpartial_db = take((size_t)L.rmax_tiles * 4);
+  }
   L.total = off;
   return L;
 }
@@ -438,9 +451,11 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
     }
   }
   mark(4);
-  uint16_t* out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
   uint8_t* sv = reinterpret_cast<uint8_t*>(saved);
   const SavedLayout SL = saved_layout(s);
+  // a training forward keeps the expert outputs for the gate-weight gradients: GEMM-2 writes them
+  // straight into the saved buffer
+  uint16_t* out_rows = reinterpret_cast<uint16_t*>(sv ? sv + SL.o : b + L.out_rows);
   float* gu_save = sv ? reinterpret_cast<float*>(sv + SL.gu) : nullptr;
   if (e == hipSuccess) {
     if (fused_gather)
@@ -475,20 +490,33 @@ moe_status forward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x,
       e = hipMemcpyAsync(sv + SL.inv, inv, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
     if (e == hipSuccess)
       e = hipMemcpyAsync(sv + SL.w, a_w, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sv + SL.assign, a_idx, (size_t)R * 4, hipMemcpyDeviceToDevice, hs);
   }
   return hip_status(e);
 }
 
+// dgate == nullptr: the expert path only (gate weights held fixed). Otherwise also dgate and, with
+// w_router, the router's gradients (dw_router, dbias) and its part of dx.
 moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, const uint16_t* dy,
                          const void* saved, const void* prepared_bwd, uint16_t* dx, void* dw_gate,
                          void* dw_up, void* dw_down, int dw_fp32, void* ws, const hipEvent_t* ev,
-                         void* stream) {
+                         void* stream, const uint16_t* w_router = nullptr, float* dgate = nullptr,
+                         float* dw_router = nullptr, float* dbias = nullptr) {
   const moe_status st = check_backward_shape(s, dt);
   if (st != MOE_OK) return st;
   if (!ok_ptr(x) || !ok_ptr(dy) || !ok_ptr(saved) || !ok_ptr(prepared_bwd) || !ok_ptr(dx) ||
       !ok_ptr(dw_gate) || !ok_ptr(dw_up) || !ok_ptr(dw_down) || !ok_ptr(ws))
     return MOE_EINVAL;
   if (dw_fp32 != 0 && dw_fp32 != 1) return MOE_EINVAL;
+  if (w_router) {
+    const moe_status rs = check_router_shape(s);
+    if (rs != MOE_OK) return rs;
+    if (!ok_ptr(w_router) || !ok_ptr(dgate) || !ok_ptr(dw_router) || !ok_opt(dbias))
+      return MOE_EINVAL;
+  } else if (dw_router || dbias) {
+    return MOE_EINVAL;
+  }
   const bool mx = dt == MOE_MXFP8;
   const int T = s->T, h = s->h, m = s->m, k = s->k, E_loc = s->E_loc, R = T * k;
   const hipStream_t hs = as_stream(stream);
@@ -500,6 +528,8 @@ moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, co
   const int32_t* inv = reinterpret_cast<const int32_t*>(sv + SL.inv);
   const float* w = reinterpret_cast<const float*>(sv + SL.w);
   const float* gu = reinterpret_cast<const float*>(sv + SL.gu);
+  const int32_t* assign = reinterpret_cast<const int32_t*>(sv + SL.assign);
+  const uint16_t* O = reinterpret_cast<const uint16_t*>(sv + SL.o);
   const PreparedBwd P = prepared_bwd_views(prepared_bwd, E_loc, h, m, mx);
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
   int32_t* koff = reinterpret_cast<int32_t*>(b + L.koff);
@@ -510,8 +540,12 @@ moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, co
   auto mark = [&](int i) {
     if (ev && e == hipSuccess) e = hipEventRecord(ev[i], hs);
   };
+  float* dl = w_router ? reinterpret_cast<float*>(b + L.dl) : nullptr;
   mark(0);
-  e = launch_kpad_table(offsets, E_loc, wgrad_k_align(mx), koff, hs);
+  // the gate weights' gradients (and the selected logits' for a router layer) first: the
+  // un-permute below adds the router's part of dx from them
+  if (dgate && e == hipSuccess) e = launch_gate_grads(dy, O, inv, w, dgate, dl, T, h, k, hs);
+  if (e == hipSuccess) e = launch_kpad_table(offsets, E_loc, wgrad_k_align(mx), koff, hs);
   if (e == hipSuccess) e = launch_gemm_tiles(offsets, b + L.tiles, R, E_loc, hs);
   mark(1);
   if (e == hipSuccess)
@@ -524,7 +558,8 @@ moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, co
                          dgu_f32, dA,
                          b + L.tiles, R, h, m, E_loc, mx, hs, ev ? ev[3] : nullptr);
   mark(4);
-  if (e == hipSuccess) e = launch_combine(dA, inv, nullptr, nullptr, dx, T, h, k, hs);
+  if (e == hipSuccess)
+    e = launch_combine(dA, inv, nullptr, nullptr, dx, T, h, k, hs, w_router, assign, dl, s->E);
   mark(5);
   const int km = L.kmax;
   if (e == hipSuccess)
@@ -545,6 +580,16 @@ moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, co
                          mx ? b + L.dGUt_s : nullptr, b + L.Ht, mx ? b + L.Ht_s : nullptr,
                          b + L.dOt, mx ? b + L.dOt_s : nullptr, koff, dw_gate, dw_up, dw_down,
                          dw_fp32 == 1, h, m, E_loc, mx, hs, ev ? ev[7] : nullptr);
+  if (w_router && e == hipSuccess) {  // the router matrix's (and bias's) gradient
+    uint8_t* rt = b + L.rtiles;
+    int* rcount = reinterpret_cast<int*>(rt);
+    int2* rtiles = reinterpret_cast<int2*>(rt + align_up(sizeof(int)));
+    e = launch_tile_table(offsets, E_loc, kRouterChunk, L.rmax_tiles, rtiles, rcount, hs);
+    if (e == hipSuccess)
+      e = launch_router_wgrad(rtiles, rcount, L.rmax_tiles, offsets, perm, dl, x, h, k, s->E,
+                              reinterpret_cast<float*>(b + L.rpartial),
+                              reinterpret_cast<float*>(b + L.rpartial_db), dw_router, dbias, hs);
+  }
   mark(8);
   return hip_status(e);
 }
@@ -604,6 +649,16 @@ moe_status moe_backward(const moe_shape* s, moe_dtype dt, const uint16_t* x, con
                         void* dw_up, void* dw_down, int dw_fp32, void* ws, void* stream) {
   return backward_impl(s, dt, x, dy, saved, prepared_bwd, dx, dw_gate, dw_up, dw_down, dw_fp32, ws,
                        nullptr, stream);
+}
+
+moe_status moe_backward_layer(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                              const uint16_t* w_router, const uint16_t* dy, const void* saved,
+                              const void* prepared_bwd, uint16_t* dx, void* dw_gate, void* dw_up,
+                              void* dw_down, int dw_fp32, float* dgate, float* dw_router,
+                              float* dbias, void* ws, void* stream) {
+  if (!ok_ptr(dgate)) return MOE_EINVAL;
+  return backward_impl(s, dt, x, dy, saved, prepared_bwd, dx, dw_gate, dw_up, dw_down, dw_fp32, ws,
+                       nullptr, stream, w_router, dgate, dw_router, dbias);
 }
 
 moe_status moe_backward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t* x,

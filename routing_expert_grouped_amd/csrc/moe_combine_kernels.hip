@@ -13,19 +13,32 @@ namespace {
 
 // KMAX: a bound on k known at compile time, so that the k row loads of a vector are all issued
 // before the first fma (a dropped slot loads a valid row and skips its fma).
-template <int KMAX>
+// ROUTER (the backward's un-permute of a router layer): after the k rows, the router's part of
+// the input gradient is added in the same fixed order, acc = fma(dl[t k + j], W_r[e_j], acc) for
+// j ascending (e_j = assign[t k + j], skipped when outside [0, E)), before the one rounding.
+template <int KMAX, bool ROUTER>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ out_rows,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w,
                                                       const uint16_t* __restrict__ shared_out,
-                                                      uint16_t* __restrict__ y, int h, int k) {
+                                                      uint16_t* __restrict__ y, int h, int k,
+                                                      const uint16_t* __restrict__ w_router,
+                                                      const int32_t* __restrict__ assign,
+                                                      const float* __restrict__ dl, int E) {
   const int t = blockIdx.x;
   int src[KMAX];
   float wt[KMAX];
+  int re[KMAX];
+  float rg[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     src[j] = j < k ? inv[(size_t)t * k + j] : -1;
     wt[j] = j < k ? (w ? w[(size_t)t * k + j] : 1.0f) : 0.0f;  // fma(1, o, acc) is the plain sum
+    if constexpr (ROUTER) {
+      const int e = j < k ? assign[(size_t)t * k + j] : -1;
+      re[j] = (unsigned)e < (unsigned)E ? e : -1;
+      rg[j] = j < k ? dl[(size_t)t * k + j] : 0.0f;
+    }
   }
   const int nv = h / 8;
   for (int v = threadIdx.x; v < nv; v += 256) {
@@ -50,6 +63,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wt[j], of[q], acc[q]);
     }
+    if constexpr (ROUTER) {
+      uint4 wr[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) wr[j] = reinterpret_cast<const uint4*>(w_router + (size_t)max(re[j], 0) * h)[v];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j >= k || re[j] < 0) continue;
+        const float rf[8] = {bf16_lo(wr[j].x), bf16_hi(wr[j].x), bf16_lo(wr[j].y),
+                             bf16_hi(wr[j].y), bf16_lo(wr[j].z), bf16_hi(wr[j].z),
+                             bf16_lo(wr[j].w), bf16_hi(wr[j].w)};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(rg[j], rf[q], acc[q]);
+      }
+    }
     uint4 r;
     r.x = pack_bf16x2(acc[0], acc[1]);
     r.y = pack_bf16x2(acc[2], acc[3]);
@@ -63,13 +91,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,
                           const uint16_t* shared_out, uint16_t* y, int T, int h, int k,
-                          hipStream_t st) {
-  if (k <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(256), 0, st, out_rows, inv, w, shared_out,
-                       y, h, k);
-  else
-    hipLaunchKernelGGL(combine_kernel<16>, dim3(T), dim3(256), 0, st, out_rows, inv, w,
-                       shared_out, y, h, k);
+                          hipStream_t st, const uint16_t* w_router, const int32_t* assign,
+                          const float* dl, int E) {
+  const dim3 g(T), b(256);
+  if (w_router) {
+    if (k <= 8)
+      hipLaunchKernelGGL((combine_kernel<8, true>), g, b, 0, st, out_rows, inv, w, shared_out, y,
+                         h, k, w_router, assign, dl, E);
+    else
+      hipLaunchKernelGGL((combine_kernel<16, true>), g, b, 0, st, out_rows, inv, w, shared_out, y,
+                         h, k, w_router, assign, dl, E);
+  } else if (k <= 8) {
+    hipLaunchKernelGGL((combine_kernel<8, false>), g, b, 0, st, out_rows, inv, w, shared_out, y,
+                       h, k, nullptr, nullptr, nullptr, 0);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<16, false>), g, b, 0, st, out_rows, inv, w, shared_out, y,
+                       h, k, nullptr, nullptr, nullptr, 0);
+  }
   return hipGetLastError();
 }
 

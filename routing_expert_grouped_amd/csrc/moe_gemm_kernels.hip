@@ -1452,6 +1452,13 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
   return hipGetLastError();
 }
 
+hipError_t launch_tile_table(const int32_t* offsets, int E_loc, int bm, int max_tiles,
+                             int2* tiles, int* tile_count, hipStream_t st) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, E_loc, bm, max_tiles,
+                     tiles, tile_count);
+  return hipGetLastError();
+}
+
 // the backward's routed-row GEMMs take 128-row tiles in both precisions (their epilogues do not
 // fit the register file next to 256-row accumulators)
 constexpr int kBwdBM = 128;

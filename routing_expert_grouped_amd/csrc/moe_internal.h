@@ -188,9 +188,32 @@ hipError_t launch_bwd_transpose(int src_kind, const void* src, const int32_t* pe
                                 int E_loc, int C, int k, int rows_max, uint8_t* dst,
                                 uint8_t* dst_s, bool mx, hipStream_t st);
 
-// Combine (moe_combine_kernels.hip); w == nullptr: every weight is 1 (the backward's un-permute)
+// Combine (moe_combine_kernels.hip); w == nullptr: every weight is 1 (the backward's un-permute).
+// w_router != nullptr (the un-permute of a router layer): the router's part of the input gradient,
+// sum_j dl[t k + j] W_r[assign[t k + j]], is added before the rounding.
 hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const float* w,
                           const uint16_t* shared_out, uint16_t* y, int T, int h, int k,
-                          hipStream_t st);
+                          hipStream_t st, const uint16_t* w_router = nullptr,
+                          const int32_t* assign = nullptr, const float* dl = nullptr, int E = 0);
+
+// Backward through the gate weights and the router (moe_router_backward_kernels.hip).
+// dgate[a] = <dY[a / k], O[inv[a]]>; with dl != nullptr also the selected-logit gradients
+// dl[a] = w[a] (dgate[a] - sum over the token's slots of w dgate)
+hipError_t launch_gate_grads(const uint16_t* dy, const uint16_t* O, const int32_t* inv,
+                             const float* w, float* dgate, float* dl, int T, int h, int k,
+                             hipStream_t st);
+// rows per chunk of the router-matrix gradient, and the chunk count bound for R rows, E experts
+constexpr int kRouterChunk = 64;
+size_t router_wgrad_tiles(int R, int E);
+// dW_r [E][h] and db [E] (or null) from dl and the rows of each expert (chunk tile table built
+// with launch_tile_table(bm = kRouterChunk)); partial: [max_tiles][h] float, partial_db [max_tiles]
+hipError_t launch_router_wgrad(const int2* tiles, const int* tile_count, int max_tiles,
+                               const int32_t* offsets, const int32_t* perm, const float* dl,
+                               const uint16_t* x, int h, int k, int E, float* partial,
+                               float* partial_db, float* dw_router, float* dbias,
+                               hipStream_t st);
+// (expert, first row) of every bm-row chunk of every expert's rows, entries past the count (-1, 0)
+hipError_t launch_tile_table(const int32_t* offsets, int E_loc, int bm, int max_tiles,
+                             int2* tiles, int* tile_count, hipStream_t st);
 
 }  // namespace moe
