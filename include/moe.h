@@ -217,6 +217,29 @@ moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                        const float* assign_w, const void* prepared, const void* shared_prepared,
                        uint16_t* y, void* saved, void* ws, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * moe_forward_ring: the forward of any number of tokens through a fixed-size buffer (the pages'
+ * macrobatch ring: "Mixture-of-Kittens" flowchart, a ring buffer of a few hundred MB; the news
+ * digest's Merged summary and the 1.41x article: a fixed-size ring token buffer cycled at
+ * minibatch granularity). The T tokens go through `ring` in consecutive minibatches of
+ * moe_forward_ring_tokens(s, dt, ring_bytes) tokens (the last one shorter); each minibatch runs
+ * moe_forward on its tokens with `ring` as its workspace, one after another on `stream`, with no
+ * host synchronisation. Every output row depends only on its own token (routing, per-token MX
+ * quantisation, per-row expert GEMMs with a fixed K order, per-token combine), so y is bitwise the
+ * y of one moe_forward over all T tokens; memory stays at ring_bytes whatever T is. Expert weights
+ * are read once per minibatch, so a ring too small for a few GEMM waves of rows per expert costs
+ * throughput, not correctness. Arguments as moe_forward (no saved state). minibatch_tokens (host,
+ * optional) receives the minibatch size. MOE_EINVAL (nothing enqueued) when even one token's
+ * minibatch does not fit.
+ * ------------------------------------------------------------------------------------------- */
+int32_t moe_forward_ring_tokens(const moe_shape* s, moe_dtype dt, size_t ring_bytes);
+moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                            const uint16_t* w_router, const float* bias, const int32_t* assign,
+                            const float* assign_w, const void* prepared,
+                            const void* shared_prepared, uint16_t* y, void* ring,
+                            size_t ring_bytes, int32_t* minibatch_tokens /* host */,
+                            void* stream);
+
 /* Profiling variant of moe_forward: the same work on the same stream, plus hipEventRecord of the
  * caller's events at the stage boundaries, so a caller can time each kernel live:
  *   ev[0] router logits ev[1] top-k ev[2] schedule ev[3] gather ev[4] tile table ev[5] GEMM-1

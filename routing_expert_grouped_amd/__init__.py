@@ -24,6 +24,7 @@ __all__ = [
     "moe_prepared_weight_bytes", "moe_prepare_weights", "moe_route", "moe_permute_workspace_bytes",
     "moe_permute", "moe_permute_static", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
+    "moe_forward_ring_tokens", "moe_forward_ring",
     "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
@@ -283,6 +284,39 @@ def moe_forward(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None, a
                                     shared_prepared, y, ws, saved, stream)
     check("moe_forward", load().moe_forward(*args, st.cuda_stream))
     return y, ws
+
+
+def moe_forward_ring_tokens(shape: MoeShape, dtype, ring_bytes: int) -> int:
+    """Tokens per minibatch of moe_forward_ring with a ring of ring_bytes bytes (0: too small)."""
+    return load().moe_forward_ring_tokens(ctypes.byref(shape), dtype_code(dtype), ring_bytes)
+
+
+def moe_forward_ring(shape: MoeShape, dtype, x, prepared, ring, w_router=None, bias=None,
+                     assign=None, assign_w=None, shared_prepared=None, y=None, stream=None):
+    """The forward of all T tokens through the fixed buffer `ring` (a uint8 CUDA tensor), in
+    minibatches of moe_forward_ring_tokens(shape, dtype, ring.numel()) tokens. Returns
+    (y, minibatch_tokens)."""
+    dt = dtype_code(dtype)
+    T, h, k, E = shape.T, shape.h, shape.k, shape.E
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        y = torch.empty(T, h, dtype=torch.bfloat16, device=_dev(x)) if y is None else y
+    nshared = 0
+    if shared_prepared is not None:
+        nshared = moe_prepared_weight_bytes(make_shape(T, h, shape.m_shared, 1, 1, 1), MOE_BF16)
+    if not ring.is_cuda or not ring.is_contiguous():
+        raise ValueError("ring: need a contiguous CUDA tensor")
+    nb = ring.numel() * ring.element_size()
+    tmb = ctypes.c_int32(0)
+    check("moe_forward_ring", load().moe_forward_ring(
+        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h),
+        _ptr(w_router, "w_router", torch.bfloat16, E * h), _ptr(bias, "bias", torch.float32, E),
+        _ptr(assign, "assign", torch.int32, T * k),
+        _ptr(assign_w, "assign_w", torch.float32, T * k),
+        _buf(prepared, "prepared", moe_prepared_weight_bytes(shape, dt)),
+        _buf(shared_prepared, "shared_prepared", nshared), _ptr(y, "y", torch.bfloat16, T * h),
+        ring.data_ptr(), nb, ctypes.byref(tmb), st.cuda_stream))
+    return y, tmb.value
 
 
 class HipEvents:

@@ -24,6 +24,7 @@ EXPORTS = [
     "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
     "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
+    "moe_forward_ring_tokens", "moe_forward_ring",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
     "moe_backward_profiled",
@@ -86,6 +87,9 @@ def load() -> ctypes.CDLL:
         "moe_forward": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P]),
         "moe_forward_profiled": (I, [S, I, P, P, P, P, P, P, P, P, P, P, P, P]),
         "moe_forward_views": (I, [S, I, P, ctypes.POINTER(MoeForwardViews)]),
+        "moe_forward_ring_tokens": (ctypes.c_int32, [S, I, Z]),
+        "moe_forward_ring": (I, [S, I, P, P, P, P, P, P, P, P, P, Z, ctypes.POINTER(ctypes.c_int32),
+                                 P]),
         "moe_saved_bytes": (Z, [S, I]),
         "moe_prepared_bwd_weight_bytes": (Z, [S, I]),
         "moe_prepare_bwd_weights": (I, [S, I, P, P, P, P, P]),

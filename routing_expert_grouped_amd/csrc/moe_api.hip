@@ -618,6 +618,49 @@ moe_status moe_forward_profiled(const moe_shape* s, moe_dtype dt, const uint16_t
                       saved, ws, reinterpret_cast<const hipEvent_t*>(events), stream);
 }
 
+int32_t moe_forward_ring_tokens(const moe_shape* s, moe_dtype dt, size_t ring_bytes) {
+  if (check_expert_shape(s, dt) != MOE_OK) return 0;
+  // forward workspace bytes grow with the token count: the largest count that fits
+  auto need = [&](int t) {
+    moe_shape sub = *s;
+    sub.T = t;
+    return moe_forward_workspace_bytes(&sub, dt);
+  };
+  if (need(1) > ring_bytes) return 0;
+  int lo = 1, hi = s->T;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (need(mid) <= ring_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                            const uint16_t* w_router, const float* bias, const int32_t* assign,
+                            const float* assign_w, const void* prepared,
+                            const void* shared_prepared, uint16_t* y, void* ring,
+                            size_t ring_bytes, int32_t* minibatch_tokens, void* stream) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(ring) || !ok_ptr(x) || !ok_ptr(y)) return MOE_EINVAL;
+  if (w_router ? (assign || assign_w) : (!ok_ptr(assign) || !ok_ptr(assign_w))) return MOE_EINVAL;
+  const int tmb = moe_forward_ring_tokens(s, dt, ring_bytes);
+  if (tmb < 1) return MOE_EINVAL;  // the ring cannot hold even one token's minibatch
+  if (minibatch_tokens) *minibatch_tokens = tmb;
+  const size_t h = (size_t)s->h, k = (size_t)s->k;
+  for (int t0 = 0; t0 < s->T; t0 += tmb) {
+    moe_shape sub = *s;
+    sub.T = std::min(tmb, s->T - t0);
+    const moe_status r = forward_impl(&sub, dt, x + t0 * h, w_router, bias,
+                                      assign ? assign + t0 * k : nullptr,
+                                      assign_w ? assign_w + t0 * k : nullptr, prepared,
+                                      shared_prepared, y + t0 * h, nullptr, ring, nullptr, stream);
+    if (r != MOE_OK) return r;
+  }
+  return MOE_OK;
+}
+
 size_t moe_saved_bytes(const moe_shape* s, moe_dtype dt) {
   if (check_backward_shape(s, dt) != MOE_OK) return 0;
   return saved_layout(s).total;

@@ -221,3 +221,29 @@ def test_permute_static_rejects_shapes_beyond_its_scratch(lib):
     assert L.moe_permute_static(ctypes.byref(small), 0, None, *args[1:], None, None) == \
         lib.MOE_EINVAL
     assert "static buffer" in L.moe_status_string(lib.MOE_ENOSCRATCH).decode()
+
+
+def test_forward_ring_minibatch_sizes(lib):
+    """moe_forward_ring_tokens is host arithmetic: the largest token count whose forward workspace
+    fits the ring (0 when one token does not), non-decreasing in the ring size, T for a ring that
+    holds the whole batch; moe_forward_ring refuses a ring that holds no minibatch before any
+    launch."""
+    L = lib.load()
+    s = _shape(lib, T=1000, h=512, m=256, E=64, k=4, E_loc=64)
+    full = L.moe_forward_workspace_bytes(ctypes.byref(s), 1)
+    assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, full) == 1000
+    assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, 1 << 40) == 1000
+    prev = 0
+    for frac in (0.05, 0.1, 0.3, 0.5, 0.9):
+        t = L.moe_forward_ring_tokens(ctypes.byref(s), 1, int(full * frac))
+        assert prev <= t < 1000
+        one = _shape(lib, T=t, h=512, m=256, E=64, k=4, E_loc=64)
+        two = _shape(lib, T=t + 1, h=512, m=256, E=64, k=4, E_loc=64)
+        assert L.moe_forward_workspace_bytes(ctypes.byref(one), 1) <= int(full * frac) < \
+            L.moe_forward_workspace_bytes(ctypes.byref(two), 1)
+        prev = t
+    assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, 1000) == 0
+    tmb = ctypes.c_int32(-1)
+    st = L.moe_forward_ring(ctypes.byref(s), 1, FAKE, FAKE, None, None, None, FAKE, None, FAKE,
+                            FAKE, 1000, ctypes.byref(tmb), None)
+    assert st == lib.MOE_EINVAL and tmb.value == -1

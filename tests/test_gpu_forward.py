@@ -204,3 +204,43 @@ def test_undersized_buffers_are_rejected_before_any_launch():
     y, _ = G.moe_forward(sh, wl.dtype, x, prepared, w_router=wr, bias=b)  # the right sizes run
     torch.cuda.synchronize()
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("name,frac", [("tiny", 0.0), ("qwen397", 0.3), ("kimi", 0.45),
+                                       ("glm52", 0.2)])
+def test_forward_ring_equals_one_forward(name, frac):
+    """moe_forward_ring (the tokens streamed through a fixed buffer in minibatches, here a fraction
+    of the one-shot workspace: several minibatches and a short last one; frac 0 = a ring that holds
+    a single token) gives bitwise the y of one moe_forward over all tokens."""
+    G = require_gpu()
+    base = I.get(name)
+    wl = I.scaled(base, **SCALED[name]) if SCALED[name] else base
+    inp = I.make_inputs(wl, seed=2)
+    wts = [I.expert_weights(wl, e, seed=2) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    shared = tuple(dev_bf16(v) for v in I.shared_weights(wl, seed=2)) if wl.m_shared else None
+    sh, y, _ = run_forward(G, wl, inp, weights, shared)
+    prepared = G.moe_prepare_weights(sh, wl.dtype, *weights)
+    sprep = None
+    if shared is not None:
+        sprep = G.moe_prepare_weights(G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1), "bf16",
+                                      *shared)
+    full = G.moe_forward_workspace_bytes(sh, wl.dtype)
+    one = G.moe_forward_workspace_bytes(
+        G.make_shape(1, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared), wl.dtype)
+    nbytes = max(one, int(full * frac)) // 256 * 256 + 256
+    ring = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    kw = {}
+    if wl.mode == "router":
+        kw["w_router"] = dev_bf16(inp["w_router"])
+        kw["bias"] = None if inp["bias"] is None else dev(inp["bias"])
+    else:
+        kw["assign"] = dev(inp["assign"])
+        kw["assign_w"] = dev(inp["assign_w"])
+    y2 = poisoned((wl.T, wl.h), torch.bfloat16)
+    y2, tmb = G.moe_forward_ring(sh, wl.dtype, dev_bf16(inp["x"]), prepared, ring,
+                                 shared_prepared=sprep, y=y2, **kw)
+    torch.cuda.synchronize()
+    note(f"ring forward {wl.describe()}: {nbytes} bytes, minibatches of {tmb} tokens")
+    assert 1 <= tmb < wl.T
+    assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))
