@@ -108,9 +108,9 @@ moe_status moe_prepare_weights(const moe_shape* s, moe_dtype dt, const uint16_t*
  *   index first on ties, -0.0 equal to +0.0; slot j holds the j-th ranked expert.
  * topk_w [T][k] float (output): exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected.
  * Requires E_loc == E. Unsupported: E > 1024 or k > 16.
- * ws: moe_route_workspace_bytes() bytes of scratch (x and w_router staged as float32, x
- *   interleaved by 8 tokens and w_router by 8 columns, so the FMAs read scalar operands and
- *   coalesced rows; the sum order above is unchanged).
+ * ws: moe_route_workspace_bytes() bytes of scratch (w_router staged as float32, interleaved by 8
+ *   columns, so a wave's row loads are contiguous; x is staged through LDS; the sum order above is
+ *   unchanged).
  * ------------------------------------------------------------------------------------------- */
 size_t moe_route_workspace_bytes(const moe_shape* s);
 moe_status moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,

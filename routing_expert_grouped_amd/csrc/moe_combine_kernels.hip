@@ -16,7 +16,7 @@ namespace {
 // ROUTER (the backward's un-permute of a router layer): after the k rows, the router's part of
 // the input gradient is added in the same fixed order, acc = fma(dl[t k + j], W_r[e_j], acc) for
 // j ascending (e_j = assign[t k + j], skipped when outside [0, E)), before the one rounding.
-template <int KMAX, bool ROUTER>
+template <int KMAX, int VPT, bool ROUTER>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ out_rows,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w,
@@ -41,49 +41,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   }
   const int nv = h / 8;
-  for (int v = threadIdx.x; v < nv; v += 256) {
-    uint4 o[KMAX];
+  // each thread takes VPT 16-byte vectors v0, v0 + 256, ... of the row and requests every row's
+  // vectors (k of them per v, plus the shared expert's) before the first fma
+  for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * VPT) {
+    uint4 o[VPT][KMAX];
+    uint4 sh[VPT];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < k) o[j] = reinterpret_cast<const uint4*>(out_rows + (size_t)max(src[j], 0) * h)[v];
-    float acc[8];
-    if (shared_out) {
-      const uint4 s = reinterpret_cast<const uint4*>(shared_out + (size_t)t * h)[v];
-      acc[0] = bf16_lo(s.x); acc[1] = bf16_hi(s.x); acc[2] = bf16_lo(s.y); acc[3] = bf16_hi(s.y);
-      acc[4] = bf16_lo(s.z); acc[5] = bf16_hi(s.z); acc[6] = bf16_lo(s.w); acc[7] = bf16_hi(s.w);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j >= k || src[j] < 0) continue;  // a dropped assignment contributes nothing
-      const float of[8] = {bf16_lo(o[j].x), bf16_hi(o[j].x), bf16_lo(o[j].y), bf16_hi(o[j].y),
-                           bf16_lo(o[j].z), bf16_hi(o[j].z), bf16_lo(o[j].w), bf16_hi(o[j].w)};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wt[j], of[q], acc[q]);
-    }
-    if constexpr (ROUTER) {
-      uint4 wr[KMAX];
+    for (int u = 0; u < VPT; ++u) {
+      const int v = v0 + 256 * u;
+      if (v >= nv) continue;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (j < k) wr[j] = reinterpret_cast<const uint4*>(w_router + (size_t)max(re[j], 0) * h)[v];
+        if (j < k) o[u][j] = reinterpret_cast<const uint4*>(out_rows + (size_t)max(src[j], 0) * h)[v];
+      if (shared_out) sh[u] = reinterpret_cast<const uint4*>(shared_out + (size_t)t * h)[v];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int v = v0 + 256 * u;
+      if (v >= nv) continue;
+      float acc[8];
+      if (shared_out) {
+        const uint4 s = sh[u];
+        acc[0] = bf16_lo(s.x); acc[1] = bf16_hi(s.x); acc[2] = bf16_lo(s.y); acc[3] = bf16_hi(s.y);
+        acc[4] = bf16_lo(s.z); acc[5] = bf16_hi(s.z); acc[6] = bf16_lo(s.w); acc[7] = bf16_hi(s.w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+      }
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
-        if (j >= k || re[j] < 0) continue;
-        const float rf[8] = {bf16_lo(wr[j].x), bf16_hi(wr[j].x), bf16_lo(wr[j].y),
-                             bf16_hi(wr[j].y), bf16_lo(wr[j].z), bf16_hi(wr[j].z),
-                             bf16_lo(wr[j].w), bf16_hi(wr[j].w)};
+        if (j >= k || src[j] < 0) continue;  // a dropped assignment contributes nothing
+        const uint4 oj = o[u][j];
+        const float of[8] = {bf16_lo(oj.x), bf16_hi(oj.x), bf16_lo(oj.y), bf16_hi(oj.y),
+                             bf16_lo(oj.z), bf16_hi(oj.z), bf16_lo(oj.w), bf16_hi(oj.w)};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(rg[j], rf[q], acc[q]);
+        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wt[j], of[q], acc[q]);
       }
+      if constexpr (ROUTER) {
+        uint4 wr[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k) wr[j] = reinterpret_cast<const uint4*>(w_router + (size_t)max(re[j], 0) * h)[v];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j >= k || re[j] < 0) continue;
+          const float rf[8] = {bf16_lo(wr[j].x), bf16_hi(wr[j].x), bf16_lo(wr[j].y),
+                               bf16_hi(wr[j].y), bf16_lo(wr[j].z), bf16_hi(wr[j].z),
+                               bf16_lo(wr[j].w), bf16_hi(wr[j].w)};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(rg[j], rf[q], acc[q]);
+        }
+      }
+      uint4 r;
+      r.x = pack_bf16x2(acc[0], acc[1]);
+      r.y = pack_bf16x2(acc[2], acc[3]);
+      r.z = pack_bf16x2(acc[4], acc[5]);
+      r.w = pack_bf16x2(acc[6], acc[7]);
+      reinterpret_cast<uint4*>(y + (size_t)t * h)[v] = r;
     }
-    uint4 r;
-    r.x = pack_bf16x2(acc[0], acc[1]);
-    r.y = pack_bf16x2(acc[2], acc[3]);
-    r.z = pack_bf16x2(acc[4], acc[5]);
-    r.w = pack_bf16x2(acc[6], acc[7]);
-    reinterpret_cast<uint4*>(y + (size_t)t * h)[v] = r;
   }
 }
 
@@ -94,20 +109,24 @@ hipError_t launch_combine(const uint16_t* out_rows, const int32_t* inv, const fl
                           hipStream_t st, const uint16_t* w_router, const int32_t* assign,
                           const float* dl, int E) {
   const dim3 g(T), b(256);
+  // vectors per thread: every 16-byte vector of the row in one round when it fits the registers
+  const int rounds = (h / 8 + 255) / 256;
+#define MOE_COMBINE(KM, VP, RT)                                                                 \
+  hipLaunchKernelGGL((combine_kernel<KM, VP, RT>), g, b, 0, st, out_rows, inv, w, shared_out, y, \
+                     h, k, w_router, assign, dl, E)
   if (w_router) {
-    if (k <= 8)
-      hipLaunchKernelGGL((combine_kernel<8, true>), g, b, 0, st, out_rows, inv, w, shared_out, y,
-                         h, k, w_router, assign, dl, E);
-    else
-      hipLaunchKernelGGL((combine_kernel<16, true>), g, b, 0, st, out_rows, inv, w, shared_out, y,
-                         h, k, w_router, assign, dl, E);
+    if (k <= 8) MOE_COMBINE(8, 1, true);
+    else MOE_COMBINE(16, 1, true);
   } else if (k <= 8) {
-    hipLaunchKernelGGL((combine_kernel<8, false>), g, b, 0, st, out_rows, inv, w, shared_out, y,
-                       h, k, nullptr, nullptr, nullptr, 0);
+    if (rounds <= 1) MOE_COMBINE(8, 1, false);
+    else if (rounds == 2) MOE_COMBINE(8, 2, false);
+    else if (rounds == 3) MOE_COMBINE(8, 3, false);
+    else MOE_COMBINE(8, 4, false);
   } else {
-    hipLaunchKernelGGL((combine_kernel<16, false>), g, b, 0, st, out_rows, inv, w, shared_out, y,
-                       h, k, nullptr, nullptr, nullptr, 0);
+    if (rounds <= 1) MOE_COMBINE(16, 1, false);
+    else MOE_COMBINE(16, 2, false);
   }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -8,45 +8,12 @@
 namespace moe {
 namespace {
 
-constexpr int kRouterTokens = 8;     // tokens per wave (held in scalar registers)
-constexpr int kRouterThreads = 256;  // one expert per lane
-
 // logits[t, e] = (((0 + x[t,0] w[e,0]) + x[t,1] w[e,1]) + ...) + bias[e], float32, one fused
 // multiply-add per step. A bf16 x bf16 product is exact in float32, so each step rounds once and
 // the order is the written left-to-right one: no split over h, no tree. Bound by the float32 FMA
-// rate, 2*T*h*E flop.
-//
-// Layout: each lane owns one expert; each workgroup owns kRouterTokens tokens whose x values are
-// wave-uniform, so they are fetched with scalar loads and fed to the FMAs as scalar operands.
-// Both operands are first staged once as float32 (exact):
-
-// x as float32, 8 tokens interleaved: xf[g][i][j] = x[8g + j][i] (zeros past T), [ceil(T/8)][h][8].
-// One thread per (group g, 8 columns): 8 16-byte loads (one per token), 256 contiguous bytes out.
-__global__ __launch_bounds__(256) void x_interleave_kernel(const uint16_t* __restrict__ x, int T,
-                                                           int h, float* __restrict__ xf) {
-  const int i8 = blockIdx.x * 256 + threadIdx.x;  // columns 8 i8 .. 8 i8 + 7
-  const int g = blockIdx.y;
-  if (8 * i8 >= h) return;
-  uint4 raw[kRouterTokens];
-#pragma unroll
-  for (int j = 0; j < kRouterTokens; ++j) {
-    const int t = g * kRouterTokens + j;
-    raw[j] = t < T ? *reinterpret_cast<const uint4*>(x + (size_t)t * h + 8 * i8)
-                   : make_uint4(0u, 0u, 0u, 0u);
-  }
-  f32x4_t* d = reinterpret_cast<f32x4_t*>(xf + ((size_t)g * h + 8 * i8) * kRouterTokens);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float v[kRouterTokens];
-#pragma unroll
-    for (int j = 0; j < kRouterTokens; ++j) {
-      const uint32_t wd = c < 2 ? raw[j].x : c < 4 ? raw[j].y : c < 6 ? raw[j].z : raw[j].w;
-      v[j] = (c & 1) ? bf16_hi(wd) : bf16_lo(wd);
-    }
-    d[2 * c] = (f32x4_t){v[0], v[1], v[2], v[3]};
-    d[2 * c + 1] = (f32x4_t){v[4], v[5], v[6], v[7]};
-  }
-}
+// rate, 2*T*h*E flop. Each lane owns one expert; the router matrix is first staged once as float32
+// (exact), interleaved by 8 columns, so a wave's loads of a step are 64 experts x 32 contiguous
+// bytes (one line per lane would thrash the vector L1: a lane's row is revisited 8 steps later).
 
 // The router matrix as float32, 8 columns of every expert side by side: wi[v][e][0..7] =
 // w[e][8v .. 8v+7], [h/8][E][8]. One thread per (e, v); 32 contiguous bytes written per thread.
@@ -61,45 +28,107 @@ __global__ __launch_bounds__(256) void w_interleave_kernel(const uint16_t* __res
   d[1] = (f32x4_t){bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
 }
 
-// The same logits, in the same order, from the interleaved float32 x and router matrix:
-//  - the 64 scalar operands of a step of 8 columns are 256 contiguous bytes (scalar loads, no
-//    conversion on the scalar unit, which otherwise issues as many instructions as the FMAs);
-//  - a wave's router-matrix loads of a step are 64 experts x 32 bytes, contiguous (16 cache
-//    lines instead of one line per lane, which thrashed the vector L1: a lane's row is revisited
-//    only 8 steps later).
-__global__ __launch_bounds__(kRouterThreads) void router_logits_xf_kernel(
-    const float* __restrict__ xf, const float* __restrict__ wi, const float* __restrict__ bias,
-    float* __restrict__ logits, int T, int h, int E) {
-  const int e = blockIdx.y * kRouterThreads + threadIdx.x;
-  const int t0 = blockIdx.x * kRouterTokens;
-  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
-  const float* xg = xf + (size_t)blockIdx.x * h * kRouterTokens;
-  float acc[kRouterTokens];
-#pragma unroll
-  for (int tt = 0; tt < kRouterTokens; ++tt) acc[tt] = 0.0f;
+// x is staged through LDS (no float32 copy of it in HBM): a workgroup owns
+// kRouterLdsTokens tokens and 256 experts (one per lane); x is brought in kRouterCols-column chunks,
+// converted to float32 (exact) and stored per 8 columns as [8 columns][tokens] with 16 floats of
+// padding after each 8-column block (the 16-lane groups that store one block fill distinct banks),
+// double buffered. A step of 8 columns reads each column's kRouterLdsTokens values with 16-byte
+// LDS reads at a wave-uniform address (broadcast) and the lane's 8 router weights from the
+// float32 interleaved copy, requested two steps ahead. Every logit's sum keeps the order i = 0,
+// 1, ..., h-1.
+constexpr int kRouterLdsTokens = 16;
+constexpr int kRouterCols = 256;
+constexpr int kRouterBlk = 8 * kRouterLdsTokens + 16;  // floats per 8-column block, padded
 
-  const int nvec = h / 8;
-  for (int v = 0; v < nvec; ++v) {
+__global__ __launch_bounds__(256) void router_logits_lds_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wi, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int h, int E) {
+  constexpr int TOK = kRouterLdsTokens;
+  constexpr int CC = kRouterCols;
+  constexpr int NBLK = CC / 8;                  // 8-column blocks per chunk
+  constexpr int PIECES = TOK * NBLK / 256;      // 16-byte x pieces per thread per chunk
+  static_assert(PIECES * 256 == TOK * NBLK, "whole pieces per thread");
+  __shared__ __attribute__((aligned(16))) float xs[2][NBLK * kRouterBlk];
+  const int tid = threadIdx.x;
+  const int e = blockIdx.y * 256 + tid;
+  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
+  const int t0 = blockIdx.x * TOK;
+  const int nch = (h + CC - 1) / CC;
+  const int nsteps = h / 8;
+
+  // piece p = tid + 256 i: token p % TOK, 8-column block p / TOK (consecutive lanes: consecutive
+  // tokens of one block, so the stores of a 16-lane group land in 16 consecutive banks)
+  uint4 raw[PIECES];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = tid + 256 * i, tt = p % TOK, b8 = p / TOK;
+      const int col = c * CC + 8 * b8, t = t0 + tt;
+      raw[i] = (t < T && col < h) ? *reinterpret_cast<const uint4*>(x + (size_t)t * h + col)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = tid + 256 * i, tt = p % TOK, b8 = p / TOK;
+      float* d = xs[buf] + b8 * kRouterBlk + tt;
+      const uint4 r = raw[i];
+      d[0 * TOK] = bf16_lo(r.x); d[1 * TOK] = bf16_hi(r.x);
+      d[2 * TOK] = bf16_lo(r.y); d[3 * TOK] = bf16_hi(r.y);
+      d[4 * TOK] = bf16_lo(r.z); d[5 * TOK] = bf16_hi(r.z);
+      d[6 * TOK] = bf16_lo(r.w); d[7 * TOK] = bf16_hi(r.w);
+    }
+  };
+  auto wrow = [&](int v, f32x4_t& w0, f32x4_t& w1) {
     const f32x4_t* wp = reinterpret_cast<const f32x4_t*>(wi + ((size_t)v * E + e_ld) * 8);
-    const f32x4_t w0 = wp[0], w1 = wp[1];
-    const float wf[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-    const float* xs = xg + (size_t)v * 8 * kRouterTokens;
+    w0 = wp[0];
+    w1 = wp[1];
+  };
+
+  float acc[TOK];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+  for (int tt = 0; tt < TOK; ++tt) acc[tt] = 0.0f;
+  fetch(0);
+  put(0);
+  __syncthreads();
+  f32x4_t wa0, wa1, wb0, wb1;  // router weights of steps v and v + 1
+  wrow(0, wa0, wa1);
+  if (nsteps > 1) wrow(1, wb0, wb1);
+  int v = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) fetch(c + 1);
+    const int vend = min(nsteps, (c + 1) * CC / 8);
+    for (; v < vend; ++v) {
+      const float wf[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
+      wa0 = wb0;
+      wa1 = wb1;
+      if (v + 2 < nsteps) wrow(v + 2, wb0, wb1);
+      const float* xb = xs[buf] + (v - c * CC / 8) * kRouterBlk;
 #pragma unroll
-      for (int tt = 0; tt < kRouterTokens; ++tt)
-        acc[tt] = __builtin_fmaf(xs[q * kRouterTokens + tt], wf[q], acc[tt]);
+      for (int q = 0; q < 8; ++q) {
+        f32x4_t xv[TOK / 4];
+#pragma unroll
+        for (int u = 0; u < TOK / 4; ++u)
+          xv[u] = *reinterpret_cast<const f32x4_t*>(xb + q * TOK + 4 * u);
+#pragma unroll
+        for (int tt = 0; tt < TOK; ++tt) acc[tt] = __builtin_fmaf(xv[tt / 4][tt % 4], wf[q], acc[tt]);
+      }
+    }
+    if (c + 1 < nch) {
+      put(buf ^ 1);  // the other buffer was last read in chunk c - 1, before this chunk's barrier
+      __syncthreads();
+    }
   }
   if (e < E) {
     const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int tt = 0; tt < kRouterTokens; ++tt) {
+    for (int tt = 0; tt < TOK; ++tt)
       if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = bias ? acc[tt] + b : acc[tt];
-    }
   }
 }
 
-// "a ranks before b": larger logit first, then the lower expert index.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
@@ -172,24 +201,19 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 }  // namespace
 
 size_t router_xf_bytes(int T, int h, int E) {
-  const size_t xf = (size_t)((T + kRouterTokens - 1) / kRouterTokens) * kRouterTokens * h * 4;
-  return align_up(xf) + (size_t)E * h * 4;
+  (void)T;
+  return (size_t)E * h * 4;  // the router matrix as float32, interleaved by 8 columns
 }
 
 hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, const float* bias,
                                    float* logits, int T, int h, int E, float* scratch,
                                    hipStream_t st) {
-  const int groups = (T + kRouterTokens - 1) / kRouterTokens;
-  float* xf = scratch;
-  float* wi = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(scratch) +
-                                       align_up((size_t)groups * kRouterTokens * h * 4));
-  hipLaunchKernelGGL(x_interleave_kernel, dim3((h / 8 + 255) / 256, groups), dim3(256), 0, st, x,
-                     T, h, xf);
+  float* wi = scratch;
   hipLaunchKernelGGL(w_interleave_kernel, dim3((E + 255) / 256, h / 8), dim3(256), 0, st, w_router,
                      E, h, wi);
-  dim3 grid(groups, (E + kRouterThreads - 1) / kRouterThreads);
-  hipLaunchKernelGGL(router_logits_xf_kernel, grid, dim3(kRouterThreads), 0, st, xf, wi, bias,
-                     logits, T, h, E);
+  dim3 grid((T + kRouterLdsTokens - 1) / kRouterLdsTokens, (E + 255) / 256);
+  hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(256), 0, st, x, wi, bias, logits, T, h,
+                     E);
   return hipGetLastError();
 }
 

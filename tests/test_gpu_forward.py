@@ -244,3 +244,36 @@ def test_forward_ring_equals_one_forward(name, frac):
     note(f"ring forward {wl.describe()}: {nbytes} bytes, minibatches of {tmb} tokens")
     assert 1 <= tmb < wl.T
     assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y2))
+
+
+def test_forward_bitwise_under_a_concurrent_busy_kernel():
+    """Bitwise determinism regardless of hardware scheduling: the forward of the GLM-5.2-shaped
+    layer (scaled) run while a long float32 kernel keeps a second stream of the same priority busy
+    (so the workgroups of both share the CUs in whatever order the hardware picks) gives bitwise
+    the y, logits and schedule of a run on an idle GPU."""
+    G = require_gpu()
+    wl = I.scaled(I.get("glm52"), T=1024, h=1024, m=512, E=64, E_loc=64)
+    inp = I.make_inputs(wl, seed=11)
+    wts = [I.expert_weights(wl, e, seed=11) for e in range(wl.E_loc)]
+    weights = tuple(dev_bf16(np.stack([w[i] for w in wts])) for i in range(3))
+    sh, y_idle, ws_idle = run_forward(G, wl, inp, weights)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in G.moe_forward_views(sh, wl.dtype, ws_idle).items()
+           if v is not None and k in ("logits", "topk_idx", "perm", "inv", "offsets")}
+    busy = torch.cuda.Stream()  # default priority, like the current stream
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.float32)
+    b = torch.randn(4096, 4096, device="cuda", dtype=torch.float32)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(busy):
+            c = a
+            for _ in range(6):
+                c = torch.matmul(c, b) * 1e-3
+        y = poisoned((wl.T, wl.h), torch.bfloat16)
+        _, y, ws = run_forward(G, wl, inp, weights, y=y)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(y), host_bf16_bits(y_idle)), rep
+        v = G.moe_forward_views(sh, wl.dtype, ws)
+        for k, r in ref.items():
+            assert torch.equal(v[k].view(torch.uint8), r.view(torch.uint8)), (rep, k)
+        del c
