@@ -43,14 +43,15 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,
   MOE_EUNSUPPORTED = 2,
   MOE_EHIP = 3,
-  MOE_ENOSCRATCH = 4 /* moe_permute_static: the shape needs more than the static scratch */
+  MOE_ENOSCRATCH = 4, /* moe_permute_static: the shape needs more than the static scratch */
+  MOE_ETIMEOUT = 5    /* moe_forward_persistent (device status word): a wait ran out of time */
 } moe_status;
 
 /* Expert GEMM precision. MOE_MXFP8: E4M3 elements with one E8M0 scale per 32 consecutive elements
@@ -239,6 +240,29 @@ moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,
                             const void* shared_prepared, uint16_t* y, void* ring,
                             size_t ring_bytes, int32_t* minibatch_tokens /* host */,
                             void* stream);
+
+/* -------------------------------------------------------------------------------------------
+ * moe_forward_persistent: the same forward as moe_forward, in one persistent kernel (the pages'
+ * megakernel: Mixture-of-Kittens page, TL;DR and flowchart, where the SMs hand work to each other
+ * through local counters rather than global barriers; news digest, Merged summary, on a schedule
+ * that never waits for the CPU). One workgroup per CU takes work items (token blocks, assignment
+ * chunks, GEMM tiles) from per-XCD queues in step order; GEMM-2 on an M tile starts as soon as
+ * that tile's GEMM-1 N tiles are done, and a token's combine as soon as its rows' GEMM-2 tiles
+ * are. Preceded by one small kernel that clears the queues and counters in ws.
+ *
+ * Arguments as moe_forward, without saved state or a shared expert. y is bitwise moe_forward's y.
+ * status: device int32, set to MOE_OK by the launch and to MOE_ETIMEOUT if an internal wait
+ * exceeded its bound (timeout_ms, wall clock; then y is undefined): read it after the stream
+ * has finished. ws: moe_forward_persistent_workspace_bytes(). Shapes: h % 256 == 0,
+ * m % 128 == 0 (2m % 256 == 0), k <= 16, else MOE_EUNSUPPORTED; m_shared > 0: MOE_EUNSUPPORTED.
+ * The kernel needs every queue served: the launch has one workgroup per CU of the device.
+ * ------------------------------------------------------------------------------------------- */
+size_t moe_forward_persistent_workspace_bytes(const moe_shape* s, moe_dtype dt);
+moe_status moe_forward_persistent(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                  const uint16_t* w_router, const float* bias,
+                                  const int32_t* assign, const float* assign_w,
+                                  const void* prepared, uint16_t* y, void* ws, int32_t* status,
+                                  int32_t timeout_ms, void* stream);
 
 /* Profiling variant of moe_forward: the same work on the same stream, plus hipEventRecord of the
  * caller's events at the stage boundaries, so a caller can time each kernel live:

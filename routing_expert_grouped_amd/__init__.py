@@ -25,6 +25,7 @@ __all__ = [
     "moe_permute", "moe_permute_static", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "moe_forward_ring_tokens", "moe_forward_ring",
+    "moe_forward_persistent_workspace_bytes", "moe_forward_persistent",
     "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
@@ -317,6 +318,38 @@ def moe_forward_ring(shape: MoeShape, dtype, x, prepared, ring, w_router=None, b
         _buf(shared_prepared, "shared_prepared", nshared), _ptr(y, "y", torch.bfloat16, T * h),
         ring.data_ptr(), nb, ctypes.byref(tmb), st.cuda_stream))
     return y, tmb.value
+
+
+def moe_forward_persistent_workspace_bytes(shape: MoeShape, dtype) -> int:
+    return load().moe_forward_persistent_workspace_bytes(ctypes.byref(shape), dtype_code(dtype))
+
+
+def moe_forward_persistent(shape: MoeShape, dtype, x, prepared, w_router=None, bias=None,
+                           assign=None, assign_w=None, y=None, ws=None, status=None,
+                           timeout_ms: int = 2000, stream=None):
+    """The forward in one persistent kernel (no saved state, no shared expert). Returns
+    (y, ws, status): status is a 1-element int32 CUDA tensor, MOE_OK or MOE_ETIMEOUT once the
+    stream has run."""
+    dt = dtype_code(dtype)
+    T, h, k, E = shape.T, shape.h, shape.k, shape.E
+    dev = _dev(x)
+    n = moe_forward_persistent_workspace_bytes(shape, dt)
+    if n == 0:
+        raise MoeError("moe_forward_persistent_workspace_bytes", 2, "shape not covered")
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        y = torch.empty(T, h, dtype=torch.bfloat16, device=dev) if y is None else y
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if ws is None else ws
+        status = torch.empty(1, dtype=torch.int32, device=dev) if status is None else status
+    check("moe_forward_persistent", load().moe_forward_persistent(
+        ctypes.byref(shape), dt, _ptr(x, "x", torch.bfloat16, T * h),
+        _ptr(w_router, "w_router", torch.bfloat16, E * h), _ptr(bias, "bias", torch.float32, E),
+        _ptr(assign, "assign", torch.int32, T * k),
+        _ptr(assign_w, "assign_w", torch.float32, T * k),
+        _buf(prepared, "prepared", moe_prepared_weight_bytes(shape, dt)),
+        _ptr(y, "y", torch.bfloat16, T * h), _buf(ws, "ws", n),
+        _ptr(status, "status", torch.int32, 1), int(timeout_ms), st.cuda_stream))
+    return y, ws, status
 
 
 class HipEvents:

@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSCRATCH = 0, 1, 2, 3, 4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSCRATCH, MOE_ETIMEOUT = 0, 1, 2, 3, 4, 5
 MOE_PERMUTE_STATIC_SCRATCH_BYTES = 8 << 20
 MOE_BF16, MOE_MXFP8 = 0, 1
 
@@ -25,6 +25,7 @@ EXPORTS = [
     "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "moe_forward_ring_tokens", "moe_forward_ring",
+    "moe_forward_persistent_workspace_bytes", "moe_forward_persistent",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
     "moe_backward_profiled",
@@ -90,6 +91,8 @@ def load() -> ctypes.CDLL:
         "moe_forward_ring_tokens": (ctypes.c_int32, [S, I, Z]),
         "moe_forward_ring": (I, [S, I, P, P, P, P, P, P, P, P, P, Z, ctypes.POINTER(ctypes.c_int32),
                                  P]),
+        "moe_forward_persistent_workspace_bytes": (Z, [S, I]),
+        "moe_forward_persistent": (I, [S, I, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P]),
         "moe_saved_bytes": (Z, [S, I]),
         "moe_prepared_bwd_weight_bytes": (Z, [S, I]),
         "moe_prepare_bwd_weights": (I, [S, I, P, P, P, P, P]),

@@ -201,6 +201,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_EHIP: return "MOE_EHIP: HIP launch error";
     case MOE_ENOSCRATCH:
       return "MOE_ENOSCRATCH: the shape needs more scratch than the static buffer holds";
+    case MOE_ETIMEOUT: return "MOE_ETIMEOUT: a device-side wait ran out of time";
   }
   return "unknown moe_status";
 }
@@ -659,6 +660,135 @@ moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,
     if (r != MOE_OK) return r;
   }
   return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct PersistentLayout {
+  ForwardLayout f;
+  size_t xf, etile, sync, args, total;
+  int bm;
+};
+
+// the forward workspace, plus its own float32 router matrix (the forward's may share the routed-row
+// buffer, which the persistent kernel fills while the router still runs), the first tile of each
+// expert and the synchronisation words
+PersistentLayout persistent_layout(const moe_shape* s, moe_dtype dt, bool router) {
+  PersistentLayout P{};
+  P.f = forward_layout(s, dt, router);
+  const int R = s->T * s->k;
+  size_t off = P.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  P.xf = router ? take(router_xf_bytes(s->T, s->h, s->E)) : 0;
+  P.bm = kPersistentRows;
+  P.etile = take((size_t)(s->E_loc + 1) * 4);
+  P.sync = take(persistent_sync_ints(R, s->E_loc, P.bm) * 4);
+  P.args = take(persistent_args_bytes());
+  P.total = off;
+  return P;
+}
+
+moe_status check_persistent_shape(const moe_shape* s, moe_dtype dt) {
+  const moe_status st = check_expert_shape(s, dt);
+  if (st != MOE_OK) return st;
+  if (s->m_shared > 0 || !ffn_big(s->h, s->m)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct DeviceFacts {
+  int num_cu = 0;
+  int clock_khz = 0;  // wall clock
+};
+std::mutex g_facts_mu;
+DeviceFacts g_facts[kMaxDevices];
+
+bool device_facts(DeviceFacts& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  DeviceFacts& f = g_facts[dev];
+  if (!f.num_cu) {
+    int cu = 0, clk = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&clk, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        cu < 1 || clk < 1)
+      return false;
+    f.num_cu = cu;
+    f.clock_khz = clk;
+  }
+  out = f;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_forward_persistent_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_persistent_shape(s, dt) != MOE_OK) return 0;
+  const bool router = s->E == s->E_loc && s->E >= s->k;
+  return persistent_layout(s, dt, router).total;
+}
+
+moe_status moe_forward_persistent(const moe_shape* s, moe_dtype dt, const uint16_t* x,
+                                  const uint16_t* w_router, const float* bias,
+                                  const int32_t* assign, const float* assign_w,
+                                  const void* prepared, uint16_t* y, void* ws, int32_t* status,
+                                  int32_t timeout_ms, void* stream) {
+  moe_status st = check_persistent_shape(s, dt);
+  if (st != MOE_OK) return st;
+  const bool router = w_router != nullptr;
+  if (router) {
+    st = check_router_shape(s);
+    if (st != MOE_OK) return st;
+    if (assign || assign_w || !ok_opt(bias)) return MOE_EINVAL;
+  } else {
+    if (!ok_ptr(assign) || !ok_ptr(assign_w) || bias) return MOE_EINVAL;
+  }
+  if (!ok_ptr(x) || !ok_ptr(prepared) || !ok_ptr(y) || !ok_ptr(ws) || !ok_ptr(status) ||
+      timeout_ms < 1)
+    return MOE_EINVAL;
+  DeviceFacts f;
+  if (!device_facts(f)) return MOE_EHIP;
+  const bool mx = dt == MOE_MXFP8;
+  const bool router_layout = s->E == s->E_loc && s->E >= s->k;
+  const PersistentLayout P = persistent_layout(s, dt, router_layout);
+  const ForwardLayout& L = P.f;
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  PersistentBuffers pb{};
+  pb.x = x;
+  pb.w_router = w_router;
+  pb.bias = bias;
+  pb.assign = assign;
+  pb.assign_w = assign_w;
+  pb.prepared = prepared;
+  pb.y = y;
+  pb.status = status;
+  pb.wi = router ? reinterpret_cast<float*>(b + P.xf) : nullptr;
+  pb.logits = router ? reinterpret_cast<float*>(b + L.logits) : nullptr;
+  pb.idx = router ? reinterpret_cast<int32_t*>(b + L.idx) : nullptr;
+  pb.tw = router ? reinterpret_cast<float*>(b + L.w) : nullptr;
+  pb.cc = reinterpret_cast<int32_t*>(b + L.sched);
+  pb.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  pb.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  pb.perm = reinterpret_cast<int32_t*>(b + L.perm);
+  pb.inv = reinterpret_cast<int32_t*>(b + L.inv);
+  pb.qrows = mx ? b + L.rows : nullptr;
+  pb.qscales = mx ? b + L.row_scales : nullptr;
+  pb.ffn_ws = b + L.ffn;
+  pb.out_rows = reinterpret_cast<uint16_t*>(b + L.out_rows);
+  pb.etile = reinterpret_cast<int32_t*>(b + P.etile);
+  pb.sync = reinterpret_cast<int*>(b + P.sync);
+  pb.args = b + P.args;
+  const long long timeout = (long long)f.clock_khz * timeout_ms;
+  return hip_status(launch_forward_persistent(pb, s->T, s->h, s->m, s->E, s->E_loc, s->k, mx,
+                                              f.num_cu, timeout, as_stream(stream)));
 }
 
 size_t moe_saved_bytes(const moe_shape* s, moe_dtype dt) {

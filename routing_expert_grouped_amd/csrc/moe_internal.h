@@ -216,4 +216,45 @@ hipError_t launch_router_wgrad(const int2* tiles, const int* tile_count, int max
 hipError_t launch_tile_table(const int32_t* offsets, int E_loc, int bm, int max_tiles,
                              int2* tiles, int* tile_count, hipStream_t st);
 
+// rows per M tile of the persistent forward's GEMMs: the 128-row large tile (its accumulators
+// leave the registers the work loop around it needs; the 192- and 256-row tiles would spill)
+constexpr int kPersistentRows = 128;
+
+// The persistent forward's buffers (device pointers; the forward workspace's, plus the float32
+// router matrix, the first tile of each expert and the synchronisation words).
+struct PersistentBuffers {
+  const uint16_t* x;
+  const uint16_t* w_router;  // null: the assignment is given
+  const float* bias;
+  const int32_t* assign;
+  const float* assign_w;
+  const void* prepared;
+  uint16_t* y;
+  int32_t* status;
+  float* wi;
+  float* logits;
+  int32_t* idx;
+  float* tw;
+  int32_t* cc;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  uint8_t* qrows;
+  uint8_t* qscales;
+  void* ffn_ws;
+  uint16_t* out_rows;
+  int32_t* etile;
+  int* sync;
+  void* args;  // persistent_args_bytes(): the kernel's argument block, in device memory
+};
+// synchronisation words of the persistent forward over R rows in bm-row tiles
+size_t persistent_sync_ints(int R, int E_loc, int bm);
+size_t persistent_args_bytes();
+// one launch of the persistent forward (after a small kernel that clears the synchronisation
+// words); num_cu workgroups, each wait bounded by `timeout` wall-clock ticks
+hipError_t launch_forward_persistent(const PersistentBuffers& b, int T, int h, int m, int E,
+                                     int E_loc, int k, bool mx, int num_cu, long long timeout,
+                                     hipStream_t st);
+
 }  // namespace moe

@@ -17,51 +17,22 @@
 //              chunk's four waves), so rows inside an expert follow the assignment order and the
 //              result never depends on scheduling.
 // Assignments with an expert id outside [0, E_loc) are dropped: they get inv = -1 and no row.
-#include "moe_internal.h"
+#include "moe_sched_body.h"
 
 namespace moe {
 namespace {
-
-constexpr int kChunk = kSchedChunk;
 
 __global__ __launch_bounds__(kChunk) void sched_count_kernel(const int32_t* __restrict__ assign,
                                                              int R, int E_loc, int nchunks,
                                                              int32_t* __restrict__ cc) {
   extern __shared__ int hist[];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E_loc; e += kChunk) hist[e] = 0;
-  __syncthreads();
-  const int a = blockIdx.x * kChunk + tid;
-  if (a < R) {
-    const int e = assign[a];
-    if ((unsigned)e < (unsigned)E_loc) atomicAdd(&hist[e], 1);
-  }
-  __syncthreads();
-  for (int e = tid; e < E_loc; e += kChunk) cc[(size_t)e * nchunks + blockIdx.x] = hist[e];
+  sched_count_chunk(assign, R, E_loc, nchunks, cc, blockIdx.x, hist);
 }
 
-// Per expert e (one wave each): the exclusive prefix of its chunk counts, in place (cc ->
-// first row of (e, chunk) relative to the expert's first row), and its total.
 __global__ __launch_bounds__(64) void sched_expert_scan_kernel(int32_t* __restrict__ cc,
                                                                 int nchunks,
                                                                 int32_t* __restrict__ counts) {
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x;
-  int32_t* row = cc + (size_t)e * nchunks;
-  int run = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += 64) {
-    const int c = c0 + lane;
-    const int x = c < nchunks ? row[c] : 0;
-    int v = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(v, off);
-      if (lane >= off) v += o;
-    }
-    if (c < nchunks) row[c] = run + v - x;
-    run += __shfl(v, 63);
-  }
-  if (lane == 0) counts[e] = run;
+  sched_expert_scan_wave(cc, nchunks, counts, blockIdx.x);
 }
 
 // Exclusive scan of the E_loc <= 1024 expert counts: offsets[0..E_loc], one workgroup of 1024.
@@ -100,40 +71,8 @@ __global__ __launch_bounds__(kChunk) void sched_rank_kernel(const int32_t* __res
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ inv) {
-  extern __shared__ int wcnt[];  // [4][E_loc]: rows of expert e taken by each wave of the chunk
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  for (int i = tid; i < 4 * E_loc; i += kChunk) wcnt[i] = 0;
-  __syncthreads();
-  const int a = blockIdx.x * kChunk + tid;
-  int e = -1;
-  if (a < R) {
-    e = assign[a];
-    if ((unsigned)e >= (unsigned)E_loc) e = -1;
-  }
-  // rank among the lanes of this wave with the same expert, by ballots over the distinct experts
-  unsigned long long todo = __ballot(e >= 0);
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int rank_w = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int e0 = __shfl(e, leader);
-    const unsigned long long same = __ballot(e == e0);
-    if (e == e0) rank_w = __builtin_popcountll(same & below);
-    if (lane == leader) wcnt[wid * E_loc + e0] = __builtin_popcountll(same);
-    todo &= ~same;
-  }
-  __syncthreads();
-  if (a < R) {
-    if (e >= 0) {
-      int r = offsets[e] + base[(size_t)e * nchunks + blockIdx.x] + rank_w;
-      for (int w = 0; w < wid; ++w) r += wcnt[w * E_loc + e];
-      perm[r] = a;
-      inv[a] = r;
-    } else {
-      inv[a] = -1;
-    }
-  }
+  extern __shared__ int wcnt[];
+  sched_rank_chunk(assign, R, E_loc, nchunks, base, offsets, perm, inv, blockIdx.x, wcnt);
 }
 
 // BF16 gather, one workgroup per token: x[t] is read once and written to its k rows.
@@ -153,57 +92,22 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
   }
 }
 
-// MXFP8 gather, one workgroup per token: each thread quantises one block of 32 values of x[t]
-// once (amax, E8M0 exponent, E4M3 codes) and writes the codes and the scale to the k rows.
-// inv == nullptr: one copy, to row t (the tokens quantised in place of the routed rows, for a
-// GEMM that gathers them itself). sc_cm_rows > 0: scales chunk-major [h/256][sc_cm_rows][8].
 __global__ __launch_bounds__(256) void gather_mxfp8_kernel(const uint16_t* __restrict__ x,
                                                            const int32_t* __restrict__ inv,
                                                            uint8_t* __restrict__ rows,
                                                            uint8_t* __restrict__ scales, int h,
                                                            int k, int sc_cm_rows) {
-  const int t = blockIdx.x;
-  const int nb = h / kMxBlock;
-  int dst[16];
-  if (!inv) k = 1;
-  for (int j = 0; j < k; ++j) dst[j] = inv ? inv[(size_t)t * k + j] : t;
-  for (int b = threadIdx.x; b < nb; b += 256) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * h + (size_t)b * kMxBlock);
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 w = src[q];
-      v[8 * q + 0] = bf16_lo(w.x);
-      v[8 * q + 1] = bf16_hi(w.x);
-      v[8 * q + 2] = bf16_lo(w.y);
-      v[8 * q + 3] = bf16_hi(w.y);
-      v[8 * q + 4] = bf16_lo(w.z);
-      v[8 * q + 5] = bf16_hi(w.z);
-      v[8 * q + 6] = bf16_lo(w.w);
-      v[8 * q + 7] = bf16_hi(w.w);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
-    const int s = mx_block_exponent(amax);
-    const float inv_s = mx_inv_scale(s);
-    uint32_t c[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      c[q] = e4m3_encode(v[4 * q] * inv_s) | (e4m3_encode(v[4 * q + 1] * inv_s) << 8) |
-             (e4m3_encode(v[4 * q + 2] * inv_s) << 16) | (e4m3_encode(v[4 * q + 3] * inv_s) << 24);
-    const uint4 lo = make_uint4(c[0], c[1], c[2], c[3]);
-    const uint4 hi = make_uint4(c[4], c[5], c[6], c[7]);
-    for (int j = 0; j < k; ++j) {
-      if (dst[j] < 0) continue;
-      uint4* d = reinterpret_cast<uint4*>(rows + (size_t)dst[j] * h + (size_t)b * kMxBlock);
-      d[0] = lo;
-      d[1] = hi;
-      const size_t so = sc_cm_rows > 0 ? ((size_t)(b >> 3) * sc_cm_rows + dst[j]) * 8 + (b & 7)
-                                       : (size_t)dst[j] * nb + b;
-      scales[so] = (uint8_t)(s + 127);
-    }
-  }
+  gather_mxfp8_token(x, inv, rows, scales, h, k, sc_cm_rows, blockIdx.x);
+}
+
+constexpr int kQuantBlocksPerThread = 4;
+
+__global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __restrict__ x,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales_cm,
+                                                              int h, int T) {
+  quantize_token_blocks<kQuantBlocksPerThread>(
+      x, codes, scales_cm, h, T, (long long)blockIdx.x * 256 * kQuantBlocksPerThread);
 }
 
 }  // namespace
@@ -242,8 +146,10 @@ hipError_t launch_gather_mxfp8(const uint16_t* x, const int32_t* inv, uint8_t* r
 
 hipError_t launch_quantize_tokens_mxfp8(const uint16_t* x, uint8_t* codes, uint8_t* scales_cm,
                                         int T, int h, hipStream_t st) {
-  hipLaunchKernelGGL(gather_mxfp8_kernel, dim3(T), dim3(256), 0, st, x, nullptr, codes,
-                     scales_cm, h, 1, T);
+  const long long blocks = (long long)T * (h / kMxBlock);
+  const long long per_wg = 256 * kQuantBlocksPerThread;
+  hipLaunchKernelGGL(quantize_tokens_kernel, dim3((unsigned)((blocks + per_wg - 1) / per_wg)),
+                     dim3(256), 0, st, x, codes, scales_cm, h, T);
   return hipGetLastError();
 }
 

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     L = lib.load()
-    assert L.moe_abi_version() == 4
-    for code in range(5):
+    assert L.moe_abi_version() == 5
+    for code in range(6):
         assert L.moe_status_string(code).decode().startswith("MOE_")
 
 
@@ -247,3 +247,30 @@ def test_forward_ring_minibatch_sizes(lib):
     st = L.moe_forward_ring(ctypes.byref(s), 1, FAKE, FAKE, None, None, None, FAKE, None, FAKE,
                             FAKE, 1000, ctypes.byref(tmb), None)
     assert st == lib.MOE_EINVAL and tmb.value == -1
+
+
+def test_persistent_forward_host_checks(lib):
+    """moe_forward_persistent: its workspace holds the forward's plus its own buffers; shapes it
+    does not cover (a shared expert, a small-tile shape) and bad arguments are refused on the host
+    before any HIP call."""
+    L = lib.load()
+    s = _shape(lib, T=300, h=768, m=512, E=64, k=8, E_loc=64)
+    for dt in (0, 1):
+        nf = L.moe_forward_workspace_bytes(ctypes.byref(s), dt)
+        npst = L.moe_forward_persistent_workspace_bytes(ctypes.byref(s), dt)
+        assert npst > nf > 0
+    shared = _shape(lib, T=64, h=512, m=256, E=8, k=2, E_loc=8, m_shared=256)
+    assert L.moe_forward_persistent_workspace_bytes(ctypes.byref(shared), 0) == 0
+    small = _shape(lib, T=64, h=384, m=128, E=8, k=2, E_loc=8)  # h % 256 != 0: small tiles
+    assert L.moe_forward_persistent_workspace_bytes(ctypes.byref(small), 0) == 0
+    args = [FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE]  # router layer
+    assert L.moe_forward_persistent(ctypes.byref(shared), 0, *args, 1000, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_forward_persistent(ctypes.byref(small), 0, *args, 1000, None) == \
+        lib.MOE_EUNSUPPORTED
+    assert L.moe_forward_persistent(ctypes.byref(s), 0, *args[:-1], None, 1000, None) == \
+        lib.MOE_EINVAL  # no status word
+    assert L.moe_forward_persistent(ctypes.byref(s), 0, *args, 0, None) == lib.MOE_EINVAL
+    both = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]  # router and an assignment
+    assert L.moe_forward_persistent(ctypes.byref(s), 0, *both, 1000, None) == lib.MOE_EINVAL
+    assert "time" in L.moe_status_string(lib.MOE_ETIMEOUT).decode()

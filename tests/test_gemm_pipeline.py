@@ -220,3 +220,20 @@ def test_replay_catches_a_wrong_count(plans):
     p3 = dict(p, scl=[p["nsc"] + 1, p["nsc"] + 1])
     with pytest.raises(AssertionError):
         replay(p3, nk)
+
+
+def test_pipelined_kernels_do_not_spill():
+    """The exact vmcnt waits of the large-tile GEMM count only its own loads: a register spill
+    inside its K loop would add scratch loads and stores. The build keeps the compiler's resource
+    report; every kernel that runs the large tile (the grouped-GEMM kernels and the persistent
+    forward) must spill no vector register."""
+    path = os.path.join(ROOT, "routing_expert_grouped_amd", "_build", "kernel_resources.json")
+    if not os.path.exists(path):
+        pytest.fail("no kernel resource report: build with `python -m routing_expert_grouped_amd.build`")
+    usage = json.load(open(path))
+    big = {k: v for k, v in usage.items()
+           if "grouped_gemm_big_kernel" in k or "forward_persistent_kernel" in k}
+    assert len(big) >= 16, sorted(usage)
+    for name, u in big.items():
+        assert u["VGPRs Spill"] == 0, (name, u)
+        assert u["LDS Size [bytes/block]"] <= 160 * 1024, (name, u)
