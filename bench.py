@@ -106,7 +106,17 @@ def stage_bytes(wl) -> dict:
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCE = os.path.join(ROOT, "routing_expert_grouped_amd", "csrc", "moe_gemm_kernels.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "routing_expert_grouped_amd", "csrc", f)
+                for f in ("moe_gemm_big.h", "moe_gemm_plan.h", "moe_gemm_kernels.hip")]
+
+
+def gemm_source_sha256() -> str:
+    """sha256 of the grouped-GEMM sources (the large-tile device code, its DMA plan and the
+    kernels), concatenated in that order: the key under which GEMM counters are kept."""
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -121,8 +131,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src:
+    if kv.get("kernel_source_sha256") != gemm_source_sha256():
         return None
     return int(kv["gemm1_bytes_per_launch"])
 
@@ -385,6 +394,43 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
     }
 
 
+def measure_persistent(G, S: Setup, steps: int, warmup: int):
+    """The same forward as one persistent kernel (moe_forward_persistent) against the plain
+    multi-kernel moe_forward (no stage events), both timed over `steps` back-to-back calls; None
+    for a shape the persistent kernel does not cover (a shared expert)."""
+    import torch
+
+    wl = S.wl
+    if wl.m_shared or G.moe_forward_persistent_workspace_bytes(S.sh, wl.dtype) == 0:
+        return None
+    yp = torch.empty_like(S.y)
+    wsp = torch.empty(G.moe_forward_persistent_workspace_bytes(S.sh, wl.dtype), dtype=torch.uint8,
+                      device=S.dev)
+    status = torch.zeros(1, dtype=torch.int32, device=S.dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms_p = timed(lambda: G.moe_forward_persistent(S.sh, wl.dtype, S.x, S.prepared, y=yp, ws=wsp,
+                                                  status=status, **S.kw))
+    ms_f = timed(lambda: G.moe_forward(S.sh, wl.dtype, S.x, S.prepared, y=S.y, ws=S.ws, **S.kw))
+    same = bool(torch.equal(yp.view(torch.int16), S.y.view(torch.int16)))
+    return {"ms_per_step": round(ms_p, 4), "multi_kernel_ms_per_step": round(ms_f, 4),
+            "status": int(status.item()), "bitwise_equal_to_multi_kernel": same}
+
+
+def progress(msg: str) -> None:
+    """One line on stderr per finished part of the run (the JSON line goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def main() -> int:
     args = parse()
     if args.copy_calibration:
@@ -407,11 +453,16 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     S = Setup(G, wl, dev, args.seed)
+    progress(f"{wl.name}: inputs and prepared weights ready")
     r = measure_forward(G, S, args.steps, args.warmup, args.flush_steps)
+    progress(f"forward timed: {r['ms_per_step']} ms per step")
+    persistent = measure_persistent(G, S, args.steps, args.warmup)
+    progress(f"persistent forward timed: {persistent}")
 
     backward = None
     if wl.backward and not args.no_backward:
         backward = time_backward(G, wl, S.sh, S.x, *S.w, S.prepared, S.kw, S.inp, args)
+        progress(f"backward timed: {backward.get('ms_per_step')} ms per step")
 
     baseline = None
     n_cpu = args.cpu_sample_tokens
@@ -437,6 +488,7 @@ def main() -> int:
                 weights_of(e)
         sh_host = tuple(host_bits(t) for t in S.shared_w) if S.shared_w is not None else None
         baseline = cpu_baseline(wl, S.inp, weights_of, sh_host, n_cpu, args.cpu_min_seconds)
+        progress(f"cpu baseline: {baseline.get('value')} {baseline.get('unit')}")
 
     others = {}
     for name in [n for n in args.others.split(",") if n]:
@@ -449,6 +501,8 @@ def main() -> int:
                                              "grouped_gemm_mfma_frac", "expert_roofline",
                                              "stages_ms")}
         others[w2.name]["dtype"] = w2.dtype
+        others[w2.name]["persistent"] = measure_persistent(G, S2, args.other_steps, 2)
+        progress(f"{w2.name}: {o['ms_per_step']} ms per step")
         del S2
         torch.cuda.empty_cache()
 
@@ -479,6 +533,7 @@ def main() -> int:
         "stages_ms": r["stages_ms"],
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
+        "persistent": persistent,
         "cpu_baseline": baseline,
         "other_workloads": others,
     }

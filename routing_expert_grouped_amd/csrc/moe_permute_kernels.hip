@@ -100,16 +100,6 @@ __global__ __launch_bounds__(256) void gather_mxfp8_kernel(const uint16_t* __res
   gather_mxfp8_token(x, inv, rows, scales, h, k, sc_cm_rows, blockIdx.x);
 }
 
-constexpr int kQuantBlocksPerThread = 4;
-
-__global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __restrict__ x,
-                                                              uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales_cm,
-                                                              int h, int T) {
-  quantize_token_blocks<kQuantBlocksPerThread>(
-      x, codes, scales_cm, h, T, (long long)blockIdx.x * 256 * kQuantBlocksPerThread);
-}
-
 }  // namespace
 
 size_t sched_workspace_bytes(int R, int E_loc) {
@@ -146,10 +136,10 @@ hipError_t launch_gather_mxfp8(const uint16_t* x, const int32_t* inv, uint8_t* r
 
 hipError_t launch_quantize_tokens_mxfp8(const uint16_t* x, uint8_t* codes, uint8_t* scales_cm,
                                         int T, int h, hipStream_t st) {
-  const long long blocks = (long long)T * (h / kMxBlock);
-  const long long per_wg = 256 * kQuantBlocksPerThread;
-  hipLaunchKernelGGL(quantize_tokens_kernel, dim3((unsigned)((blocks + per_wg - 1) / per_wg)),
-                     dim3(256), 0, st, x, codes, scales_cm, h, T);
+  // one workgroup per token (measured faster here than one flat list of blocks, which the
+  // persistent forward uses for its four-wave workgroups)
+  hipLaunchKernelGGL(gather_mxfp8_kernel, dim3(T), dim3(256), 0, st, x, nullptr, codes,
+                     scales_cm, h, 1, T);
   return hipGetLastError();
 }
 
