@@ -72,6 +72,14 @@ typedef struct {
 const char* moe_status_string(moe_status s);
 int moe_abi_version(void);
 
+/* Diagnostic: the E4M3 encoder the kernels use (the hardware conversion after a clamp to +-448)
+ * against the rounding rule of the MX definition (round to nearest even, saturate to 448, keep the
+ * sign of zero), on the current device, for every float32 of magnitude below 2^17 and both signs,
+ * plus the byte order of the four-code packing. mismatches: device int64, set to the number of
+ * inputs on which they differ (0 expected) once the stream has run. MOE_EINVAL for a null or
+ * misaligned pointer. */
+moe_status moe_check_e4m3(int64_t* mismatches, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Weight preparation (offline, not part of a forward pass).
  *

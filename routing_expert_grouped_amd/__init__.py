@@ -25,7 +25,7 @@ __all__ = [
     "moe_permute", "moe_permute_static", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine",
     "moe_forward_workspace_bytes", "moe_forward", "moe_forward_profiled", "moe_forward_views",
     "moe_forward_ring_tokens", "moe_forward_ring",
-    "moe_forward_persistent_workspace_bytes", "moe_forward_persistent",
+    "moe_forward_persistent_workspace_bytes", "moe_forward_persistent", "moe_check_e4m3",
     "HipEvents", "STAGES", "BWD_STAGES", "MOE_BWD_PROFILE_EVENTS",
     "moe_saved_bytes", "moe_prepared_bwd_weight_bytes", "moe_prepare_bwd_weights",
     "moe_backward_workspace_bytes", "moe_backward", "moe_backward_layer",
@@ -318,6 +318,17 @@ def moe_forward_ring(shape: MoeShape, dtype, x, prepared, ring, w_router=None, b
         _buf(shared_prepared, "shared_prepared", nshared), _ptr(y, "y", torch.bfloat16, T * h),
         ring.data_ptr(), nb, ctypes.byref(tmb), st.cuda_stream))
     return y, tmb.value
+
+
+def moe_check_e4m3(stream=None) -> int:
+    """Runs the library's E4M3 encoder against the rounding rule on every float32 below 2^17 on the
+    current device; returns the number of mismatching inputs (synchronises the stream)."""
+    st = _stream_obj(stream)
+    with torch.cuda.stream(st):
+        out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    check("moe_check_e4m3", load().moe_check_e4m3(out.data_ptr(), st.cuda_stream))
+    st.synchronize()
+    return int(out.item())
 
 
 def moe_forward_persistent_workspace_bytes(shape: MoeShape, dtype) -> int:

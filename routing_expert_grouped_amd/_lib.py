@@ -17,7 +17,7 @@ MOE_BF16, MOE_MXFP8 = 0, 1
 
 # every function the header declares, for the symbol check
 EXPORTS = [
-    "moe_status_string", "moe_abi_version",
+    "moe_status_string", "moe_abi_version", "moe_check_e4m3",
     "moe_prepared_weight_bytes", "moe_prepare_weights",
     "moe_route_workspace_bytes", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute", "moe_permute_static",
@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "moe_status_string": (ctypes.c_char_p, [I]),
         "moe_abi_version": (I, []),
+        "moe_check_e4m3": (I, [P, P]),
         "moe_prepared_weight_bytes": (Z, [S, I]),
         "moe_prepare_weights": (I, [S, I, P, P, P, P, P]),
         "moe_route_workspace_bytes": (Z, [S]),

@@ -208,6 +208,11 @@ const char* moe_status_string(moe_status s) {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+moe_status moe_check_e4m3(int64_t* mismatches, void* stream) {
+  if (!ok_ptr(mismatches)) return MOE_EINVAL;
+  return hip_status(launch_check_e4m3(mismatches, as_stream(stream)));
+}
+
 size_t moe_prepared_weight_bytes(const moe_shape* s, moe_dtype dt) {
   if (check_expert_shape(s, dt) != MOE_OK) return 0;
   return prepared_bytes(s->E_loc, s->h, s->m, dt == MOE_MXFP8);

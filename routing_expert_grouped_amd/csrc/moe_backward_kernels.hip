@@ -63,8 +63,7 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(const uint16_t* __restri
     uint32_t c[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      c[q] = e4m3_encode(v[4 * q] * inv) | (e4m3_encode(v[4 * q + 1] * inv) << 8) |
-             (e4m3_encode(v[4 * q + 2] * inv) << 16) | (e4m3_encode(v[4 * q + 3] * inv) << 24);
+      c[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
     uint4* d = reinterpret_cast<uint4*>(dst + kd);
     d[0] = make_uint4(c[0], c[1], c[2], c[3]);
     d[1] = make_uint4(c[4], c[5], c[6], c[7]);
@@ -148,8 +147,8 @@ __global__ __launch_bounds__(256) void uncombine_kernel(const uint16_t* __restri
       uint32_t c[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        c[q] = e4m3_encode(v[4 * q] * inv) | (e4m3_encode(v[4 * q + 1] * inv) << 8) |
-               (e4m3_encode(v[4 * q + 2] * inv) << 16) | (e4m3_encode(v[4 * q + 3] * inv) << 24);
+        c[q] = e4m3_pack4(v[4 * q] * inv, v[4 * q + 1] * inv,
+                          v[4 * q + 2] * inv, v[4 * q + 3] * inv);
       uint4* d = reinterpret_cast<uint4*>(dO + (size_t)r * h + b * kMxBlock);
       d[0] = make_uint4(c[0], c[1], c[2], c[3]);
       d[1] = make_uint4(c[4], c[5], c[6], c[7]);
@@ -280,10 +279,8 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     uint32_t cw[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      cw[q] = e4m3_encode(tile[32 * b + 4 * q][c] * inv) |
-              (e4m3_encode(tile[32 * b + 4 * q + 1][c] * inv) << 8) |
-              (e4m3_encode(tile[32 * b + 4 * q + 2][c] * inv) << 16) |
-              (e4m3_encode(tile[32 * b + 4 * q + 3][c] * inv) << 24);
+      cw[q] = e4m3_pack4(tile[32 * b + 4 * q][c] * inv, tile[32 * b + 4 * q + 1][c] * inv,
+                         tile[32 * b + 4 * q + 2][c] * inv, tile[32 * b + 4 * q + 3][c] * inv);
     uint4* d = reinterpret_cast<uint4*>(dst + col_at + 32 * b);
     d[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     d[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);

@@ -714,10 +714,8 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
             uint8_t* out = reinterpret_cast<uint8_t*>(p.out) + (size_t)r * Hn + col0;
 #pragma unroll
             for (int b4 = 0; b4 < 4; ++b4) {
-              const uint32_t w4 = e4m3_encode(hv[4 * b4 + 0] * inv) |
-                                  (e4m3_encode(hv[4 * b4 + 1] * inv) << 8) |
-                                  (e4m3_encode(hv[4 * b4 + 2] * inv) << 16) |
-                                  (e4m3_encode(hv[4 * b4 + 3] * inv) << 24);
+              const uint32_t w4 = e4m3_pack4(hv[4 * b4 + 0] * inv, hv[4 * b4 + 1] * inv,
+                                             hv[4 * b4 + 2] * inv, hv[4 * b4 + 3] * inv);
               *reinterpret_cast<uint32_t*>(out + b4 * 8 + g * 4) = w4;
             }
             if (g == 0) {
@@ -793,11 +791,9 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
               const float* a4 = dg + 4 * b4;
               const float* c4 = du + 4 * b4;
               *reinterpret_cast<uint32_t*>(out + 8 * b4) =
-                  e4m3_encode(a4[0] * ig) | (e4m3_encode(a4[1] * ig) << 8) |
-                  (e4m3_encode(a4[2] * ig) << 16) | (e4m3_encode(a4[3] * ig) << 24);
+                  e4m3_pack4(a4[0] * ig, a4[1] * ig, a4[2] * ig, a4[3] * ig);
               *reinterpret_cast<uint32_t*>(out + 32 + 8 * b4) =
-                  e4m3_encode(c4[0] * iu) | (e4m3_encode(c4[1] * iu) << 8) |
-                  (e4m3_encode(c4[2] * iu) << 16) | (e4m3_encode(c4[3] * iu) << 24);
+                  e4m3_pack4(c4[0] * iu, c4[1] * iu, c4[2] * iu, c4[3] * iu);
             }
             // scale bytes of the dG block (lane group 0) and the dU block (lane group 1)
             const int kb = (cg >> 5) + g;  // MX block along 2m

@@ -242,9 +242,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs p) {
           uint8_t* out = reinterpret_cast<uint8_t*>(p.out) + (size_t)r * Hn + col0;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            uint32_t w4 = e4m3_encode(hv[4 * b + 0] * inv) | (e4m3_encode(hv[4 * b + 1] * inv) << 8) |
-                          (e4m3_encode(hv[4 * b + 2] * inv) << 16) |
-                          (e4m3_encode(hv[4 * b + 3] * inv) << 24);
+            uint32_t w4 = e4m3_pack4(hv[4 * b + 0] * inv, hv[4 * b + 1] * inv,
+                                     hv[4 * b + 2] * inv, hv[4 * b + 3] * inv);
             *reinterpret_cast<uint32_t*>(out + b * 8 + g * 4) = w4;
           }
           if (g == 0) p.out_scales[(size_t)r * (Hn / kMxBlock) + (col0 >> 5)] = (uint8_t)(s + 127);

@@ -62,7 +62,7 @@ __device__ __forceinline__ float mx_inv_scale(int s) {
 // |y| >= 448 saturates to 448, the sign of zero is kept, NaN is never produced.
 // Normal range |y| >= 2^-6: with |y| = f * 2^e (1 <= f < 2) the mantissa is rint(|y| * 2^(3-e)) - 8,
 // a carry to 16 moves to the next binade. Below 2^-6: n = rint(|y| * 2^9), n = 8 is code 0x08.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+__device__ __forceinline__ uint32_t e4m3_encode_rule(float y) {
   uint32_t u = __float_as_uint(y);
   uint32_t sign = (u >> 24) & 0x80u;
   float a = __uint_as_float(u & 0x7fffffffu);
@@ -79,6 +79,24 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     code = ((uint32_t)(e + 7) << 3) | (n - 8u);
   }
   return code | sign;
+}
+
+// The same code from the hardware conversion: v_cvt_pk_fp8_f32 rounds to nearest even into OCP
+// E4M3 and keeps the sign of zero; the clamp to +-448 first gives the saturation. Equal to
+// e4m3_encode_rule for every float32 (a GPU test compares the two over all of them up to 2^17).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const float c = fminf(fmaxf(y, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
+}
+
+// Four codes in one word, a in the low byte: two packed conversions.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -215,6 +233,10 @@ hipError_t launch_router_wgrad(const int2* tiles, const int* tile_count, int max
 // (expert, first row) of every bm-row chunk of every expert's rows, entries past the count (-1, 0)
 hipError_t launch_tile_table(const int32_t* offsets, int E_loc, int bm, int max_tiles,
                              int2* tiles, int* tile_count, hipStream_t st);
+
+// the hardware E4M3 encoder against e4m3_encode_rule on every float32 below 2^17 (both signs),
+// and the byte order of e4m3_pack4: *mismatches (device) = the number of differing inputs
+hipError_t launch_check_e4m3(int64_t* mismatches, hipStream_t st);
 
 // rows per M tile of the persistent forward's GEMMs: the 128-row large tile (its accumulators
 // leave the registers the work loop around it needs; the 192- and 256-row tiles would spill)

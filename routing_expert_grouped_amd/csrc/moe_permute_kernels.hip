@@ -100,7 +100,34 @@ __global__ __launch_bounds__(256) void gather_mxfp8_kernel(const uint16_t* __res
   gather_mxfp8_token(x, inv, rows, scales, h, k, sc_cm_rows, blockIdx.x);
 }
 
+__global__ void zero_i64_kernel(int64_t* p) { *p = 0; }
+
+// every float32 with bits in [lo, lo + n), both signs
+__global__ __launch_bounds__(256) void check_e4m3_kernel(uint32_t lo, uint32_t n,
+                                                         int64_t* mismatches) {
+  int64_t bad = 0;
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    for (int s = 0; s < 2; ++s) {
+      const float y = __uint_as_float((lo + i) | (s ? 0x80000000u : 0u));
+      const uint32_t q = e4m3_encode_rule(y) | (e4m3_encode_rule(-y) << 8) |
+                         (e4m3_encode_rule(0.5f * y) << 16) | (e4m3_encode_rule(2.0f * y) << 24);
+      bad += (e4m3_encode(y) != e4m3_encode_rule(y)) + (e4m3_pack4(y, -y, 0.5f * y, 2.0f * y) != q);
+    }
+  }
+  if (bad) atomicAdd(reinterpret_cast<unsigned long long*>(mismatches), (unsigned long long)bad);
+}
+
 }  // namespace
+
+hipError_t launch_check_e4m3(int64_t* mismatches, hipStream_t st) {
+  hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(1), 0, st, mismatches);
+  const uint32_t ranges[][2] = {{0x00000000u, 0x00800000u}, {0x00800000u, 0x32000000u},
+                                {0x32000000u, 0x44000000u}, {0x44000000u, 0x48000000u}};
+  for (const auto& r : ranges)
+    hipLaunchKernelGGL(check_e4m3_kernel, dim3(4096), dim3(256), 0, st, r[0], r[1] - r[0],
+                       mismatches);
+  return hipGetLastError();
+}
 
 size_t sched_workspace_bytes(int R, int E_loc) {
   const int nchunks = (R + kChunk - 1) / kChunk;

@@ -118,8 +118,8 @@ __device__ __forceinline__ int mx_quantize_block32(const uint4 (&w)[4], uint4& l
   uint32_t c[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    c[q] = e4m3_encode(v[4 * q] * inv_s) | (e4m3_encode(v[4 * q + 1] * inv_s) << 8) |
-           (e4m3_encode(v[4 * q + 2] * inv_s) << 16) | (e4m3_encode(v[4 * q + 3] * inv_s) << 24);
+    c[q] = e4m3_pack4(v[4 * q] * inv_s, v[4 * q + 1] * inv_s,
+                      v[4 * q + 2] * inv_s, v[4 * q + 3] * inv_s);
   lo = make_uint4(c[0], c[1], c[2], c[3]);
   hi = make_uint4(c[4], c[5], c[6], c[7]);
   return s;
