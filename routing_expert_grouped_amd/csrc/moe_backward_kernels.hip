@@ -248,8 +248,8 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
         const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gu + gcol + 36);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[j] = g0[j] / (1.0f + expf(-g0[j])) * u0[j];
-          v[4 + j] = g1[j] / (1.0f + expf(-g1[j])) * u1[j];
+          v[j] = silu_f(g0[j]) * u0[j];
+          v[4 + j] = silu_f(g1[j]) * u1[j];
         }
       } else {
         const float* sp = reinterpret_cast<const float*>(src_) + (size_t)r * C + c0 + cq;

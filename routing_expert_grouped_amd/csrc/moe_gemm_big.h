@@ -90,7 +90,6 @@ __device__ __forceinline__ f32x16_t mfma_mx_sel(int sel, const i32x8_t& a, const
   }
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // ------------------------------------------------------------------------------------------------
 // Large-tile grouped GEMM: 256 weight rows x BM routed rows (BM = 256 or 128) per workgroup of 4
@@ -766,7 +765,7 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float dh = acc[i][j][4 * b4 + q];
-            const float sg = 1.0f / (1.0f + expf(-G[q]));
+            const float sg = sigmoid_f(G[q]);
             const float silu = G[q] * sg;
             const float dsilu = sg * (1.0f + G[q] * (1.0f - sg));
             dg[4 * b4 + q] = dh * U[q] * dsilu;

@@ -58,6 +58,16 @@ __device__ __forceinline__ float mx_inv_scale(int s) {
                 : __uint_as_float((uint32_t)e << 23);
 }
 
+// The logistic function 1 / (1 + e^-z) with the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about one ulp each): e^-z = 2^(-z log2 e). For z far below zero the
+// exponential overflows to +inf and the result is 0; far above, 2^-big is 0 and the result 1.
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// silu(z) = z * sigmoid(z)
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
+
 // E4M3 code of y (already divided by the block scale): round to nearest, ties to even mantissa,
 // |y| >= 448 saturates to 448, the sign of zero is kept, NaN is never produced.
 // Normal range |y| >= 2^-6: with |y| = f * 2^e (1 <= f < 2) the mantissa is rint(|y| * 2^(3-e)) - 8,
