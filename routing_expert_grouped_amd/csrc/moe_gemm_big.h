@@ -729,11 +729,16 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
       }
     }
   } else if constexpr (MODE == kEpiStore) {
+    // The bf16 tile goes out through LDS, so that each store instruction writes whole 128-byte
+    // lines (16 bytes per lane, two rows of 512 bytes per wave) instead of 16 bytes of 32 rows.
+    // Every DMA load and every fragment read of the main loop is complete before LDS is reused.
+    constexpr int RS = BN * 2 + 16;  // LDS row stride in bytes (256 bf16 + 16 bytes of padding)
+    static_assert(BM * RS <= NS * WSTAGE + NSR * RSTAGE, "the output tile fits the rings' LDS");
+    wait_vmcnt<0>();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int r = row0 + (BM / 2) * wm + 32 * j + li;
-      if (r >= row_end) continue;
-      uint16_t* out = reinterpret_cast<uint16_t*>(p.out) + (size_t)r * p.N + n0 + 128 * wn;
+      uint8_t* lrow = lds + ((BM / 2) * wm + 32 * j + li) * RS + 2 * (128 * wn + 4 * g);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -741,8 +746,19 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
           uint2 v;
           v.x = pack_bf16x2(acc[i][j][4 * b4 + 0], acc[i][j][4 * b4 + 1]);
           v.y = pack_bf16x2(acc[i][j][4 * b4 + 2], acc[i][j][4 * b4 + 3]);
-          *reinterpret_cast<uint2*>(out + 32 * i + b4 * 8 + g * 4) = v;
+          *reinterpret_cast<uint2*>(lrow + 2 * (32 * i + 8 * b4)) = v;
         }
+    }
+    lds_barrier();
+    const int c16 = tid & 31;  // 16-byte chunk of the row: output columns n0 + 8 c16 .. + 8
+#pragma unroll
+    for (int rr0 = 0; rr0 < BM; rr0 += 8) {
+      const int rr = rr0 + (tid >> 5);
+      const int r = row0 + rr;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + rr * RS + 16 * c16);
+      if (r < row_end)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)r * p.N + n0 +
+                                  8 * c16) = v;
     }
   } else if constexpr (MODE == kEpiDSwiglu) {
     // N = m dH columns. The 32-column tile i starting at column nb is one block of dG and one of
