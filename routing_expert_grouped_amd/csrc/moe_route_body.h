@@ -34,7 +34,7 @@ __device__ __forceinline__ void w_interleave_one(const uint16_t* __restrict__ w,
 // LDS reads at a wave-uniform address (broadcast) and the lane's 8 router weights from the
 // float32 interleaved copy, requested two steps ahead. Every logit's sum keeps the order i = 0,
 // 1, ..., h-1.
-constexpr int kRouterLdsTokens = 16;  // tokens per workgroup of the router kernel
+constexpr int kRouterLdsTokens = 8;  // tokens per workgroup of the router kernel
 constexpr int kRouterCols = 256;
 // floats per 8-column block of TOK tokens, padded
 __host__ __device__ constexpr int router_blk(int tok) { return 8 * tok + 16; }
@@ -44,9 +44,14 @@ __host__ __device__ constexpr int router_lds_floats(int tok) {
   return 2 * (kRouterCols / 8) * router_blk(tok);
 }
 
-// Tokens [bx * TOK, +TOK) x experts [by * 256, +256) by one workgroup of 256 threads, through
-// router_lds_floats(TOK) floats of LDS at xs_lds.
-template <int TOK>
+// Tokens [bx * TOK, +TOK) x experts [by * NT * EPL, +NT * EPL) by one workgroup of NT threads,
+// through router_lds_floats(TOK) floats of LDS at xs_lds. Thread l owns experts
+// by * NT * EPL + l + NT * u (u < EPL): each x value read from LDS feeds EPL fused multiply-adds
+// (one float of LDS per FMA would need 256 bytes per clock per CU at the FMA rate; the LDS
+// returns about 100-190). The router kernel takes 8 tokens and two experts per thread (0.44 ms on
+// the GLM-5.2-shaped layer against 0.50 with 16 tokens and one expert, 0.70 with 16 and two: its
+// grid then has only two waves per SIMD).
+template <int TOK, int NT = 256, int EPL = 1>
 __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ wi,
                                                    const float* __restrict__ bias,
@@ -55,23 +60,29 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
   constexpr int CC = kRouterCols;
   constexpr int BLK = router_blk(TOK);
   constexpr int NBLK = CC / 8;                  // 8-column blocks per chunk
-  constexpr int PIECES = TOK * NBLK / 256;      // 16-byte x pieces per thread per chunk
-  static_assert(PIECES * 256 == TOK * NBLK, "whole pieces per thread");
+  constexpr int PIECES = TOK * NBLK / NT;       // 16-byte x pieces per thread per chunk
+  static_assert(PIECES * NT == TOK * NBLK, "whole pieces per thread");
+  static_assert((CC / 8) % 2 == 0, "chunks of an even number of steps");
+  static_assert(TOK % 8 == 0, "tokens in groups of 8");
   auto xs = [&](int buf) { return xs_lds + buf * (NBLK * BLK); };
   const int tid = threadIdx.x;
-  const int e = by * 256 + tid;
-  const int e_ld = e < E ? e : E - 1;  // idle lanes read a valid row and store nothing
+  int e[EPL], e_ld[EPL];
+#pragma unroll
+  for (int u = 0; u < EPL; ++u) {
+    e[u] = by * NT * EPL + tid + NT * u;
+    e_ld[u] = e[u] < E ? e[u] : E - 1;  // idle lanes read a valid row and store nothing
+  }
   const int t0 = bx * TOK;
   const int nch = (h + CC - 1) / CC;
   const int nsteps = h / 8;
 
-  // piece p = tid + 256 i: token p % TOK, 8-column block p / TOK (consecutive lanes: consecutive
+  // piece p = tid + NT i: token p % TOK, 8-column block p / TOK (consecutive lanes: consecutive
   // tokens of one block, so the stores of a 16-lane group land in 16 consecutive banks)
   uint4 raw[PIECES];
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
-      const int p = tid + 256 * i, tt = p % TOK, b8 = p / TOK;
+      const int p = tid + NT * i, tt = p % TOK, b8 = p / TOK;
       const int col = c * CC + 8 * b8, t = t0 + tt;
       raw[i] = (t < T && col < h) ? *reinterpret_cast<const uint4*>(x + (size_t)t * h + col)
                                   : make_uint4(0u, 0u, 0u, 0u);
@@ -80,7 +91,7 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
-      const int p = tid + 256 * i, tt = p % TOK, b8 = p / TOK;
+      const int p = tid + NT * i, tt = p % TOK, b8 = p / TOK;
       float* d = xs(buf) + b8 * BLK + tt;
       const uint4 r = raw[i];
       d[0 * TOK] = bf16_lo(r.x); d[1 * TOK] = bf16_hi(r.x);
@@ -89,52 +100,101 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
       d[6 * TOK] = bf16_lo(r.w); d[7 * TOK] = bf16_hi(r.w);
     }
   };
-  auto wrow = [&](int v, f32x4_t& w0, f32x4_t& w1) {
-    const f32x4_t* wp = reinterpret_cast<const f32x4_t*>(wi + ((size_t)v * E + e_ld) * 8);
-    w0 = wp[0];
-    w1 = wp[1];
+  // the 8 router weights of step v for each owned expert
+  auto wrow = [&](int v, f32x4_t (&w)[EPL][2]) {
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) {
+      const f32x4_t* wp = reinterpret_cast<const f32x4_t*>(wi + ((size_t)v * E + e_ld[u]) * 8);
+      w[u][0] = wp[0];
+      w[u][1] = wp[1];
+    }
   };
 
-  float acc[TOK];
+  float acc[EPL][TOK];
 #pragma unroll
-  for (int tt = 0; tt < TOK; ++tt) acc[tt] = 0.0f;
+  for (int u = 0; u < EPL; ++u)
+#pragma unroll
+    for (int tt = 0; tt < TOK; ++tt) acc[u][tt] = 0.0f;
+  // step v (8 columns) from the LDS block at xb with the weights w of step v, which are then
+  // reloaded with those of step v + 2; the x values of column q + 1 are read while column q's
+  // multiply-adds run
+  auto step = [&](int v, const float* xb, f32x4_t (&w)[EPL][2]) {
+    float wf[EPL][8];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wf[u][q] = w[u][0][q];
+        wf[u][4 + q] = w[u][1][q];
+      }
+    if (v + 2 < nsteps) wrow(v + 2, w);
+    f32x4_t xa[TOK / 4], xn[TOK / 4];
+#pragma unroll
+    for (int i = 0; i < TOK / 4; ++i) xa[i] = *reinterpret_cast<const f32x4_t*>(xb + 4 * i);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < TOK / 4; ++i)
+          xn[i] = *reinterpret_cast<const f32x4_t*>(xb + (q + 1) * TOK + 4 * i);
+      }
+#pragma unroll
+      for (int u = 0; u < EPL; ++u)
+#pragma unroll
+        for (int tt = 0; tt < TOK; ++tt)
+          acc[u][tt] = __builtin_fmaf(xa[tt / 4][tt % 4], wf[u][q], acc[u][tt]);
+#pragma unroll
+      for (int i = 0; i < TOK / 4; ++i) xa[i] = xn[i];
+      // this column's multiply-adds stay here and no LDS read moves above (or merges across)
+      // them: two columns of x in registers
+#pragma unroll
+      for (int u = 0; u < EPL; ++u)
+#pragma unroll
+        for (int tt = 0; tt < TOK; tt += 8)
+          asm volatile("" : "+v"(acc[u][tt]), "+v"(acc[u][tt + 1]), "+v"(acc[u][tt + 2]),
+                       "+v"(acc[u][tt + 3]), "+v"(acc[u][tt + 4]), "+v"(acc[u][tt + 5]),
+                       "+v"(acc[u][tt + 6]), "+v"(acc[u][tt + 7])::"memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   fetch(0);
   put(0);
   __syncthreads();
-  f32x4_t wa0, wa1, wb0, wb1;  // router weights of steps v and v + 1
-  wrow(0, wa0, wa1);
-  if (nsteps > 1) wrow(1, wb0, wb1);
+  // router weights of the even steps in wa, of the odd steps in wb (each reloaded two steps
+  // ahead, so no register copies wait on a load just issued)
+  f32x4_t wa[EPL][2], wb[EPL][2];
+  wrow(0, wa);
+  if (nsteps > 1) wrow(1, wb);
   int v = 0;
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
     if (c + 1 < nch) fetch(c + 1);
     const int vend = min(nsteps, (c + 1) * CC / 8);
-    for (; v < vend; ++v) {
-      const float wf[8] = {wa0[0], wa0[1], wa0[2], wa0[3], wa1[0], wa1[1], wa1[2], wa1[3]};
-      wa0 = wb0;
-      wa1 = wb1;
-      if (v + 2 < nsteps) wrow(v + 2, wb0, wb1);
-      const float* xb = xs(buf) + (v - c * CC / 8) * BLK;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        f32x4_t xv[TOK / 4];
-#pragma unroll
-        for (int u = 0; u < TOK / 4; ++u)
-          xv[u] = *reinterpret_cast<const f32x4_t*>(xb + q * TOK + 4 * u);
-#pragma unroll
-        for (int tt = 0; tt < TOK; ++tt) acc[tt] = __builtin_fmaf(xv[tt / 4][tt % 4], wf[q], acc[tt]);
-      }
+    const int v0 = c * (CC / 8);  // the chunk's first step: its block 0 in the buffer
+    // a chunk starts at an even step (CC / 8 is even), so pairs never straddle chunks; an odd
+    // last step is even-numbered
+    for (; v + 1 < vend; v += 2) {
+      step(v, xs(buf) + (v - v0) * BLK, wa);
+      step(v + 1, xs(buf) + (v + 1 - v0) * BLK, wb);
+    }
+    if (v < vend) {
+      step(v, xs(buf) + (v - v0) * BLK, wa);
+      ++v;
     }
     if (c + 1 < nch) {
       put(buf ^ 1);  // the other buffer was last read in chunk c - 1, before this chunk's barrier
       __syncthreads();
     }
   }
-  if (e < E) {
-    const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int tt = 0; tt < TOK; ++tt)
-      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = bias ? acc[tt] + b : acc[tt];
+  for (int u = 0; u < EPL; ++u) {
+    if (e[u] < E) {
+      const float b = bias ? bias[e[u]] : 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < TOK; ++tt)
+        if (t0 + tt < T)
+          logits[(size_t)(t0 + tt) * E + e[u]] = bias ? acc[u][tt] + b : acc[u][tt];
+    }
   }
 }
 

@@ -13,11 +13,15 @@ __global__ __launch_bounds__(256) void w_interleave_kernel(const uint16_t* __res
   w_interleave_one(w, E, h, wi, blockIdx.x * 256 + threadIdx.x, blockIdx.y);
 }
 
-__global__ __launch_bounds__(256) void router_logits_lds_kernel(
+// 128 threads, two experts per thread: 256 experts per workgroup
+constexpr int kRouterThreads = 128;
+constexpr int kRouterEpl = 2;
+__global__ __launch_bounds__(kRouterThreads) void router_logits_lds_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wi, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int h, int E) {
   __shared__ __attribute__((aligned(16))) float xs[router_lds_floats(kRouterLdsTokens)];
-  router_logits_tile<kRouterLdsTokens>(x, wi, bias, logits, T, h, E, blockIdx.x, blockIdx.y, xs);
+  router_logits_tile<kRouterLdsTokens, kRouterThreads, kRouterEpl>(x, wi, bias, logits, T, h, E,
+                                                                    blockIdx.x, blockIdx.y, xs);
 }
 
 // one wave per token
@@ -43,9 +47,10 @@ hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, 
   float* wi = scratch;
   hipLaunchKernelGGL(w_interleave_kernel, dim3((E + 255) / 256, h / 8), dim3(256), 0, st, w_router,
                      E, h, wi);
-  dim3 grid((T + kRouterLdsTokens - 1) / kRouterLdsTokens, (E + 255) / 256);
-  hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(256), 0, st, x, wi, bias, logits, T, h,
-                     E);
+  constexpr int ew = kRouterThreads * kRouterEpl;  // experts per workgroup
+  dim3 grid((T + kRouterLdsTokens - 1) / kRouterLdsTokens, (E + ew - 1) / ew);
+  hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(kRouterThreads), 0, st, x, wi, bias,
+                     logits, T, h, E);
   return hipGetLastError();
 }
 
