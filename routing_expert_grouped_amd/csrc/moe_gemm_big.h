@@ -844,35 +844,55 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
       }
     }
   } else {  // kEpiWgrad: out[e][r][n] of an M x N matrix per expert (or split gate / up halves)
+    // Staged through LDS as float32, half of the tile's rows at a time (the waves of row half wm
+    // write theirs, then all 256 threads store them), so that the stores write whole lines: a row
+    // of the tile is 256 outputs, 64 chunks of 4; with split_gate_up, chunk c of a row is output
+    // column 4 (c % 32) of the gate half (c < 32) or the up half, i.e. tile column
+    // 64 ((c % 32) / 8) + 32 (c / 32) + 4 (c % 8), since the N index alternates 32 gate and 32 up
+    // columns.
+    constexpr int RSW = BN * 4 + 16;  // LDS row stride in bytes (256 floats + 16 bytes of padding)
+    static_assert((BM / 2) * RSW <= NS * WSTAGE + NSR * RSTAGE, "half a tile fits the rings' LDS");
+    const int ld = p.split_gate_up ? (p.N >> 1) : p.N;
+    const size_t ebase = (size_t)e * p.M * ld;
+    wait_vmcnt<0>();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int nb = n0 + 128 * wn + 32 * i;
-      void* o = p.out;
-      int col = nb, ld = p.N;
-      if (p.split_gate_up) {  // N index: blocks of 32 alternate gate and up columns
-        o = ((nb >> 5) & 1) ? p.out2 : p.out;
-        col = (nb >> 6) * 32;
-        ld = p.N >> 1;
+    for (int half = 0; half < 2; ++half) {
+      lds_barrier();  // the main loop's (or the previous half's) LDS reads are done
+      if (wm == half) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          uint8_t* lrow = lds + (32 * j + li) * RSW + 4 * (128 * wn + 4 * g);
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4)
+              *reinterpret_cast<f32x4_t*>(lrow + 4 * (32 * i + 8 * b4)) =
+                  (f32x4_t){acc[i][j][4 * b4], acc[i][j][4 * b4 + 1], acc[i][j][4 * b4 + 2],
+                            acc[i][j][4 * b4 + 3]};
+        }
       }
-      const size_t ebase = (size_t)e * p.M * ld;
+      lds_barrier();
+      const int c = tid & 63;  // chunk of 4 outputs
+      int lcol = 4 * c;
+      void* o = p.out;
+      int col = n0 + 4 * c;
+      if (p.split_gate_up) {
+        const int hc = c >> 5, j4 = c & 31;
+        lcol = 64 * (j4 >> 3) + 32 * hc + 4 * (j4 & 7);
+        o = hc ? p.out2 : p.out;
+        col = (n0 >> 1) + 4 * j4;
+      }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int r = row0 + (BM / 2) * wm + 32 * j + li;
-        const size_t at = ebase + (size_t)r * ld + col + 4 * g;
+      for (int rr0 = 0; rr0 < BM / 2; rr0 += 4) {
+        const int rr = rr0 + (tid >> 6);
+        const int r = row0 + (BM / 2) * half + rr;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lds + rr * RSW + 4 * lcol);
+        const size_t at = ebase + (size_t)r * ld + col;
         if (p.out_f32) {
-          float* of = reinterpret_cast<float*>(o) + at;
-#pragma unroll
-          for (int b4 = 0; b4 < 4; ++b4)
-            *reinterpret_cast<f32x4_t*>(of + 8 * b4) =
-                (f32x4_t){acc[i][j][4 * b4], acc[i][j][4 * b4 + 1], acc[i][j][4 * b4 + 2],
-                          acc[i][j][4 * b4 + 3]};
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(o) + at) = v;
         } else {
-          uint16_t* ob = reinterpret_cast<uint16_t*>(o) + at;
-#pragma unroll
-          for (int b4 = 0; b4 < 4; ++b4)
-            *reinterpret_cast<uint2*>(ob + 8 * b4) =
-                make_uint2(pack_bf16x2(acc[i][j][4 * b4], acc[i][j][4 * b4 + 1]),
-                           pack_bf16x2(acc[i][j][4 * b4 + 2], acc[i][j][4 * b4 + 3]));
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + at) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
