@@ -363,7 +363,20 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
             for k, v in ev.stage_ms().items():
                 flushed[k] += v / flush_steps
             ev.close()
-        del scratch
+        # the practical HBM ceiling of this GPU for the bandwidth stages: a plain 1 GiB device
+        # copy (read + write bytes over its event time)
+        dst = torch.empty_like(scratch)
+        dst.copy_(scratch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(scratch)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = round(2 * 5 * scratch.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del scratch, dst
+    else:
+        copy_gbs = None
     for ev in events + [warm_ev]:
         ev.close()
     counts = G.moe_forward_views(S.sh, wl.dtype, S.ws)["counts"].cpu().numpy()
@@ -389,6 +402,7 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         "stages_gbs": {k: gbs(k, stages) for k in ("gather", "combine", "topk")},
         "stages_gbs_flushed": ({k: gbs(k, flushed) for k in ("gather", "combine", "topk")}
                                if flush_steps > 0 else None),
+        "hbm_copy_gbs": copy_gbs,
         "router_tflops": (round(fl["router"] / (stages["router_logits"] * 1e-3) / 1e12, 1)
                           if fl["router"] and stages["router_logits"] > 0 else None),
     }
@@ -533,6 +547,7 @@ def main() -> int:
         "stages_ms": r["stages_ms"],
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
+        "hbm_copy_gbs": r["hbm_copy_gbs"],
         "persistent": persistent,
         "cpu_baseline": baseline,
         "other_workloads": others,
