@@ -440,6 +440,50 @@ def measure_persistent(G, S: Setup, steps: int, warmup: int):
             "status": int(status.item()), "bitwise_equal_to_multi_kernel": same}
 
 
+def library_dense_gemms(wl, dev) -> dict:
+    """Context, not part of the path: the vendor library's dense GEMM (torch -> hipBLASLt) at the
+    grouped GEMMs' shapes taken as one product over all routed rows, [R x K] by one [K x N] weight
+    (GEMM-1: K = h, N = 2m; GEMM-2: K = m, N = h), in BF16, or for MXFP8 in FP8 E4M3 with one
+    scale per tensor (torch._scaled_mm; the library has no block-scaled path here). One weight
+    matrix stays in the caches, the grouped GEMMs stream every expert's weights."""
+    import torch
+
+    R = wl.T * wl.k
+    out = {"dtype": ("fp8 e4m3, per-tensor scale" if wl.dtype == "mxfp8" else "bf16"),
+           "shapes": {"gemm1": [R, 2 * wl.m, wl.h], "gemm2": [R, wl.h, wl.m]}}
+    for name, (M, N, K) in (("gemm1", (R, 2 * wl.m, wl.h)), ("gemm2", (R, wl.h, wl.m))):
+        try:
+            if wl.dtype == "mxfp8":
+                A = (torch.randn(M, K, device=dev) * 0.5).to(torch.float8_e4m3fn)
+                B = (torch.randn(N, K, device=dev) * 0.5).to(torch.float8_e4m3fn)
+                one = torch.ones((), device=dev)
+
+                def f():
+                    return torch._scaled_mm(A, B.t(), scale_a=one, scale_b=one,
+                                            out_dtype=torch.bfloat16)
+            else:
+                A = torch.randn(M, K, device=dev).to(torch.bfloat16)
+                B = torch.randn(N, K, device=dev).to(torch.bfloat16)
+
+                def f():
+                    return A @ B.t()
+            for _ in range(3):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name + "_ms"] = round(e0.elapsed_time(e1) / 10, 4)
+            del A, B
+        except Exception as exc:  # a library without this path: report, do not fail the bench
+            out[name + "_ms"] = None
+            out[name + "_error"] = repr(exc)[:200]
+    torch.cuda.empty_cache()
+    return out
+
+
 def progress(msg: str) -> None:
     """One line on stderr per finished part of the run (the JSON line goes to stdout)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -472,6 +516,8 @@ def main() -> int:
     progress(f"forward timed: {r['ms_per_step']} ms per step")
     persistent = measure_persistent(G, S, args.steps, args.warmup)
     progress(f"persistent forward timed: {persistent}")
+    library = library_dense_gemms(wl, dev)
+    progress(f"library dense GEMMs: {library}")
 
     backward = None
     if wl.backward and not args.no_backward:
@@ -548,6 +594,7 @@ def main() -> int:
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
         "hbm_copy_gbs": r["hbm_copy_gbs"],
+        "library_dense_gemm": library,
         "persistent": persistent,
         "cpu_baseline": baseline,
         "other_workloads": others,
