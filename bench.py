@@ -326,9 +326,11 @@ class Setup:
 
 
 def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> dict:
-    """Times `steps` back-to-back forwards (after `warmup`), every stage with HIP events; then
-    `flush_steps` forwards each preceded by a 1 GiB write (outside the stage events) for the
-    bandwidth stages' GB/s with the last-level cache flushed."""
+    """Times `steps` back-to-back forwards (moe_forward, after `warmup`): ms_per_step. Then the
+    same number of profiled forwards (moe_forward_profiled, the same launches with a HIP event at
+    every stage boundary, which cost a few µs each) for the stage times; then `flush_steps`
+    forwards each preceded by a 1 GiB write (outside the stage events) for the bandwidth stages'
+    GB/s with the last-level cache flushed."""
     import torch
 
     wl = S.wl
@@ -337,16 +339,26 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         G.moe_forward_profiled(S.sh, wl.dtype, S.x, S.prepared, ev, shared_prepared=S.shared_prep,
                                y=S.y, ws=S.ws, **S.kw)
 
+    def plain():
+        G.moe_forward(S.sh, wl.dtype, S.x, S.prepared, shared_prepared=S.shared_prep, y=S.y,
+                      ws=S.ws, **S.kw)
+
     events = [G.HipEvents() for _ in range(steps)]
     warm_ev = G.HipEvents()
     for _ in range(warmup):
         step(warm_ev)
+        plain()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plain()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
     t0 = time.perf_counter()
     for ev in events:
         step(ev)
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    profiled_ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = {k: 0.0 for k in G.STAGES}
     for ev in events:
         for k, v in ev.stage_ms().items():
@@ -392,6 +404,7 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
     return {
         "tokens_per_s": round(wl.T / (ms_per_step * 1e-3), 1),
         "ms_per_step": round(ms_per_step, 4),
+        "profiled_ms_per_step": round(profiled_ms, 4),
         "gemm1_tflops": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12, 1),
         "gemm1_mfma_frac": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12 / peak, 4),
         "grouped_gemm_mfma_frac": round((fl["gemm1"] + fl["gemm2"]) / ((g1_ms + g2_ms) * 1e-3)
@@ -484,6 +497,42 @@ def library_dense_gemms(wl, dev) -> dict:
     return out
 
 
+def measure_graph(G, S: Setup, steps: int, warmup: int) -> dict:
+    """The same forward captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed: the
+    launch sequence is recorded, so each step is one graph launch (what a serving loop over small
+    batches would run). Its output is compared bitwise with the eager forward's."""
+    import torch
+
+    wl = S.wl
+    Y = torch.empty_like(S.y)
+
+    def fwd():
+        G.moe_forward(S.sh, wl.dtype, S.x, S.prepared, shared_prepared=S.shared_prep, y=Y,
+                      ws=S.ws, **S.kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = Y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    same = bool(torch.equal(Y.view(torch.int16), ref.view(torch.int16)))
+    del g
+    return {"ms_per_step": round(ms, 4), "bitwise_equal_to_eager": same}
+
+
 def progress(msg: str) -> None:
     """One line on stderr per finished part of the run (the JSON line goes to stdout)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -516,6 +565,8 @@ def main() -> int:
     progress(f"forward timed: {r['ms_per_step']} ms per step")
     persistent = measure_persistent(G, S, args.steps, args.warmup)
     progress(f"persistent forward timed: {persistent}")
+    graph = measure_graph(G, S, args.steps, args.warmup)
+    progress(f"graph-replayed forward timed: {graph}")
     library = library_dense_gemms(wl, dev)
     progress(f"library dense GEMMs: {library}")
 
@@ -557,11 +608,13 @@ def main() -> int:
             continue
         S2 = Setup(G, w2, dev, args.seed)
         o = measure_forward(G, S2, args.other_steps, 2, 0)
-        others[w2.name] = {k: o[k] for k in ("tokens_per_s", "ms_per_step", "gemm1_mfma_frac",
+        others[w2.name] = {k: o[k] for k in ("tokens_per_s", "ms_per_step",
+                                             "profiled_ms_per_step", "gemm1_mfma_frac",
                                              "grouped_gemm_mfma_frac", "expert_roofline",
                                              "stages_ms")}
         others[w2.name]["dtype"] = w2.dtype
         others[w2.name]["persistent"] = measure_persistent(G, S2, args.other_steps, 2)
+        others[w2.name]["graph"] = measure_graph(G, S2, args.other_steps, 2)
         progress(f"{w2.name}: {o['ms_per_step']} ms per step")
         del S2
         torch.cuda.empty_cache()
@@ -590,12 +643,14 @@ def main() -> int:
         "grouped_gemm_mfma_frac": r["grouped_gemm_mfma_frac"],
         "layer_tflops": r["layer_tflops"],
         "router_tflops": r["router_tflops"],
+        "profiled_ms_per_step": r["profiled_ms_per_step"],
         "stages_ms": r["stages_ms"],
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
         "hbm_copy_gbs": r["hbm_copy_gbs"],
         "library_dense_gemm": library,
         "persistent": persistent,
+        "graph": graph,
         "cpu_baseline": baseline,
         "other_workloads": others,
     }
