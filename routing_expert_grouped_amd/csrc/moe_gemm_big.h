@@ -241,7 +241,12 @@ __device__ __forceinline__ bool big_tile_coords(int mt_total, int Nt, int x, int
 // (expert, M tile) pair for weight gradients) by N tile nt, computed by the calling workgroup's 256
 // threads through the LDS rings at `lds` (big_lds_bytes). Returns with every DMA load of the tile
 // complete; the caller separates two tiles on the same LDS by a barrier.
-template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
+//
+// PIPE = false: the fragments of a k-step are read from LDS right before its MFMAs instead of
+// during the previous k-step's (one set of fragment registers instead of two), for a kernel that
+// runs two workgroups per CU, where the other workgroup's MFMAs cover the LDS latency. The DMA
+// issue order, and so every wait count, is the one of the pipelined loop.
+template <int MODE, bool MX, int BM, int RB, int NS, int NSR, bool PIPE = true>
 __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, uint8_t* lds) {
   constexpr int BN = kBigBN;
   constexpr int WSTAGE = BN * RB;                // one stage of the weight operand
@@ -514,13 +519,43 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
   //      stores zeros; the condition is uniform over the workgroup)
   Frags FA, FB;
   if (MODE != kEpiWgrad || nk > 0) {
-  if constexpr (MX) {
+  if constexpr (MX && PIPE) {
     sload(0, nscw, nscr);
   }
 #pragma unroll
   for (int b = -(NDEEP - 1); b < 0; ++b)
 #pragma unroll
     for (int part = 0; part < SPS; ++part) issue_part(b, part);
+  if constexpr (!PIPE) {
+    // stage j: its wait and barrier (point j); at a chunk's first stage the chunk's scale words,
+    // read here with ordinary loads the compiler waits for itself (in a loop, untracked loads
+    // whose registers the compiler may copy or reuse while they are in flight are not safe; they
+    // sit where the pipelined loop issues the next chunk's words, so the counted waits only get
+    // stricter); then point j's DMA groups, and per k-step the fragments and MFMAs
+    for (int j = 0; j < nk; ++j) {
+      barrier_point(j);
+      if constexpr (MX) {
+        if (j % PC == 0) {
+          const uint32_t cc = (uint32_t)(j / PC);
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            scw[i] = scale_word(*reinterpret_cast<const uint64_t*>(wsb + sw_off[i] + w_cs * cc));
+#pragma unroll
+          for (int q = 0; q < NJ; ++q)
+            scr[q] = scale_word(*reinterpret_cast<const uint64_t*>(rsb + sr_off[q] + r_cs * cc));
+        }
+      }
+#pragma unroll
+      for (int part = 0; part < SPS; ++part) issue_part(j, part);
+#pragma unroll
+      for (int t = 0; t < SPS; ++t) {
+        Frags F;
+        load_frags(F, j, t);
+#pragma unroll
+        for (int k = 0; k < NM; ++k) mfma_k(F, k, (j % PC) * SPS + t);
+      }
+    }
+  } else {
   barrier_point(0);
   if constexpr (MX) take_scales();
   load_frags(FA, 0, 0);
@@ -660,6 +695,7 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
   const int jsteady = plan_steady_end(PO::get(), nk);
   run(0, jsteady, std::true_type{});
   run(jsteady, nk, std::false_type{});
+  }  // PIPE
   }  // nk > 0
 
   // ---- epilogue. acc[i][j][q]: weight row n0 + 128 wn + 32 i + 8 (q / 4) + 4 g + q % 4,
@@ -901,12 +937,12 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
 
 
 // the tile of workgroup jx of XCD x (big_tile_coords); none for a surplus workgroup
-template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
+template <int MODE, bool MX, int BM, int RB, int NS, int NSR, bool PIPE = true>
 __device__ __forceinline__ void big_tile(const GemmArgs& p, int x, int jx, uint8_t* lds) {
   const int mt_total = MODE == kEpiWgrad ? p.tiles_total : *p.tile_count;
   int ti, nt;
   if (!big_tile_coords(mt_total, p.N / kBigBN, x, jx, ti, nt)) return;  // before any barrier
-  big_tile_at<MODE, MX, BM, RB, NS, NSR>(p, ti, nt, lds);
+  big_tile_at<MODE, MX, BM, RB, NS, NSR, PIPE>(p, ti, nt, lds);
 }
 
 }  // namespace

@@ -277,6 +277,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_big_kernel(GemmArgs p) {
   big_tile<MODE, MX, BM, RB, NS, NSR>(p, blockIdx.x & 7, blockIdx.x >> 3, lds);
 }
 
+// The same with two workgroups per CU (at most 80 KB of LDS and 256 registers each, fragments
+// read per k-step): the weight gradients, whose tiles reduce over a short K and end in a large
+// float32 store, so one workgroup's stores drain while the other's loads and MFMAs run.
+template <int MODE, bool MX, int BM, int RB, int NS, int NSR>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_big_kernel_occ2(GemmArgs p) {
+  static_assert(big_lds_bytes(BM, RB, NS, NSR) <= 80 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[big_lds_bytes(BM, RB, NS, NSR)];
+  big_tile<MODE, MX, BM, RB, NS, NSR, false>(p, blockIdx.x & 7, blockIdx.x >> 3, lds);
+}
+
 // One workgroup: M tiles of bm rows per expert from the device-side offsets, written as
 // (expert, first row) entries; entries past the total are (-1, 0).
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets,
@@ -509,6 +519,12 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
 #define MOE_BIG(MODEV, MXV, BMV, G, A)                                                          \
   hipLaunchKernelGGL((grouped_gemm_big_kernel<MODEV, MXV, BMV, kBigRB, big_ns(MXV, BMV),        \
                                               big_nsr(MXV, BMV)>),                              \
+                     G, dim3(256), 0, st, A)
+
+// weight gradients: 64-row tiles, two-deep rings, two workgroups per CU (moe_gemm_plan.h)
+#define MOE_BIG_OCC2(MODEV, MXV, G, A)                                                          \
+  hipLaunchKernelGGL((grouped_gemm_big_kernel_occ2<MODEV, MXV, kWgradRows, kBigRB, kWgradNS,    \
+                                                   kWgradNSR>),                                 \
                      G, dim3(256), 0, st, A)
 
 // grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most
@@ -746,7 +762,7 @@ hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_
                             void* dw_gate, void* dw_up, void* dw_down, bool out_f32, int h, int m,
                             int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid) {
   if (h % kBigBN || m % kBigBN) return hipErrorInvalidValue;
-  const int bm = mx ? 128 : 256;
+  const int bm = kWgradRows;
   // dW_gate | dW_up [e] (h x 2m) = A_e^T [dG | dU]_e: M side A^T (h rows), N side [dG | dU]^T
   GemmArgs a{};
   a.rows = At;
@@ -779,14 +795,15 @@ hipError_t launch_bwd_wgrad(const uint8_t* At, const uint8_t* At_s, const uint8_
   b.w_sc_cm = b.r_sc_cm = mx ? 1 : 0;
   b.sc_rows = m;
   const dim3 ga = big_grid(a.tiles_total, a.N / kBigBN), gb = big_grid(b.tiles_total, b.N / kBigBN);
-  if (mx) MOE_BIG(kEpiWgrad, true, 128, ga, a);
-  else MOE_BIG(kEpiWgrad, false, 256, ga, a);
+  if (mx) MOE_BIG_OCC2(kEpiWgrad, true, ga, a);
+  else MOE_BIG_OCC2(kEpiWgrad, false, ga, a);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
-  if (mx) MOE_BIG(kEpiWgrad, true, 128, gb, b);
-  else MOE_BIG(kEpiWgrad, false, 256, gb, b);
+  if (mx) MOE_BIG_OCC2(kEpiWgrad, true, gb, b);
+  else MOE_BIG_OCC2(kEpiWgrad, false, gb, b);
   return hipGetLastError();
 }
 
 #undef MOE_BIG
+#undef MOE_BIG_OCC2
 
 }  // namespace moe

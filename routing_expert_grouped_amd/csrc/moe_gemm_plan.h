@@ -147,4 +147,10 @@ MOE_HD constexpr int big_ns(bool mx, int bm) { return (void)mx, (void)bm, 3; }
 MOE_HD constexpr int big_nsr(bool mx, int bm) { return (void)mx, bm >= 192 ? 2 : 4; }
 #define MOE_BIG_TILE_CONFIGS(X) X(true, 192) X(true, 128) X(false, 256) X(false, 128)
 
+// The weight gradients' tile: 64 rows with two-deep rings (80 KB of LDS), two workgroups per CU,
+// fragments read per k-step (no software pipelining; the DMA issue order is the generic loop's)
+constexpr int kWgradRows = 64;
+constexpr int kWgradNS = 2;
+constexpr int kWgradNSR = 2;
+
 }  // namespace moe

@@ -53,15 +53,19 @@ static void dump(bool mx, int bm, int ns, int nsr, bool inst) {
 #define INST(MX, BM) dump(MX, BM, big_ns(MX, BM), big_nsr(MX, BM), true);
 int main() {
   MOE_BIG_TILE_CONFIGS(INST)
+  // the weight gradients' unpipelined two-workgroup tile (replayed in both program orders)
+  dump(true, kWgradRows, kWgradNS, kWgradNSR, true);
+  dump(false, kWgradRows, kWgradNS, kWgradNSR, true);
   // every other ring-depth pair the plan supports within the LDS budget
   const bool mxs[2] = {true, false};
-  const int bms[3] = {128, 192, 256};
+  const int bms[4] = {64, 128, 192, 256};
   for (bool mx : mxs)
     for (int bm : bms)
       for (int ns = 2; ns <= 5; ++ns)
         for (int nsr = ns - 1; nsr <= ns + 1; ++nsr) {
           if (nsr < 2 || (ns * 256 + nsr * bm) * 128 > 160 * 1024) continue;
           if (mx && bm == 256) continue;  // does not fit the register file
+          if (bm == kWgradRows && ns == kWgradNS && nsr == kWgradNSR) continue;  // listed above
           dump(mx, bm, ns, nsr, false);
         }
   return 0;
@@ -176,6 +180,65 @@ def replay(p, nk):
         assert issued.get(("W", s)) == p["qw"] and issued.get(("R", s)) == p["qr"], s
 
 
+def replay_unpipelined(p, nk):
+    """The unpipelined loop (PIPE = false): stage j waits at its own barrier point, then (a
+    chunk's first stage) loads that chunk's scale words with ordinary loads the compiler waits for
+    itself, then issues all of point j's DMA parts; the fragments are read after that (LDS only,
+    not counted). No scale words go out in the prologue."""
+    ns, nsr, sps, pc, nsc = p["ns"], p["nsr"], p["sps"], p["pc"], p["nsc"]
+    mx = bool(p["mx"])
+    parts, is_w = p["parts"], p["w"]
+    waits = p["counts"][str(nk)][1:]
+    nchunks = nk // pc if mx else 0
+    seq, last, issued = [], {}, {}
+    state = {"barrier": 0, "done": 0, "pending": None}
+
+    def dma(kind, s):
+        prev = s - (ns if kind == "W" else nsr)
+        if prev >= 0:
+            assert state["barrier"] >= prev + 1, f"{kind}({s}) overwrites stage {prev} before it is read"
+        last[(kind, s)] = len(seq)
+        issued[(kind, s)] = issued.get((kind, s), 0) + 1
+        seq.append((kind, s))
+
+    def issue_part(b, t):
+        for q in range(parts[t], parts[t + 1]):
+            kind = "W" if is_w[q] else "R"
+            s = b + (ns if kind == "W" else nsr) - 1
+            if 0 <= s < nk:
+                dma(kind, s)
+
+    for b in range(-(max(ns, nsr) - 1), 0):
+        for t in range(sps):
+            issue_part(b, t)
+    for j in range(nk):
+        n = waits[j]
+        assert 0 <= n and n + (nsc if mx else 0) < 64, (j, n)
+        state["done"] = max(state["done"], len(seq) - n)
+        assert issued.get(("W", j), 0) == p["qw"] and issued.get(("R", j), 0) == p["qr"], j
+        assert max(last[("W", j)], last[("R", j)]) < state["done"], f"stage {j} in flight"
+        state["barrier"] = j
+        if mx and j % pc == 0:
+            seq.extend([("S", j // pc)] * nsc)  # waited for by the compiler before their use
+            state["done"] = len(seq)
+        for t in range(sps):
+            issue_part(j, t)
+    for s in range(nk):
+        assert issued.get(("W", s)) == p["qw"] and issued.get(("R", s)) == p["qr"], s
+
+
+def test_unpipelined_weight_gradient_tile(plans):
+    """The two-workgroup weight-gradient tile waits with the plan's counts in the unpipelined
+    program order, for every K length."""
+    sel = [q for q in plans if q["inst"] and q["bm"] == 64]
+    assert len(sel) == 2
+    for p in sel:
+        for nk in range(1, NK_MAX + 1):
+            if p["mx"] and nk % p["pc"]:
+                continue
+            replay_unpipelined(p, nk)
+
+
 def test_plan_covers_every_instantiation(plans):
     """Every (MXFP8, tile height) the launchers instantiate is in MOE_BIG_TILE_CONFIGS."""
     text = open(KERNELS).read()
@@ -185,6 +248,8 @@ def test_plan_covers_every_instantiation(plans):
         used.add((mx == "true", int(consts.get(bm, bm))))
     listed = {(bool(p["mx"]), p["bm"]) for p in plans if p["inst"]}
     assert used and used <= listed, used - listed
+    # the two-workgroup kernel takes the weight gradients' constants, listed above
+    assert "MOE_BIG_OCC2(" in text and "kWgradRows, kBigRB, kWgradNS" in text
 
 
 @pytest.mark.parametrize("which", ["instantiated", "other depths"])
