@@ -533,6 +533,42 @@ def measure_graph(G, S: Setup, steps: int, warmup: int) -> dict:
     return {"ms_per_step": round(ms, 4), "bitwise_equal_to_eager": same}
 
 
+def measure_ring(G, S: Setup, steps: int, warmup: int) -> list:
+    """moe_forward_ring: all T tokens streamed through a fixed buffer of a fraction of the one-shot
+    workspace (the pages' macrobatch ring), in minibatches of the largest token count that fits;
+    step time and whether y equals the one-shot forward bitwise."""
+    import torch
+
+    wl = S.wl
+    full = G.moe_forward_workspace_bytes(S.sh, wl.dtype)
+    ref = S.y.clone()
+    out = []
+    for frac in (0.5, 0.25, 0.125):
+        nbytes = int(full * frac) // 256 * 256
+        ring = torch.empty(nbytes, dtype=torch.uint8, device=S.dev)
+        y = torch.empty_like(S.y)
+
+        def run():
+            return G.moe_forward_ring(S.sh, wl.dtype, S.x, S.prepared, ring,
+                                      shared_prepared=S.shared_prep, y=y, **S.kw)[1]
+
+        for _ in range(warmup):
+            tmb = run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out.append({"ring_bytes": nbytes, "fraction_of_workspace": frac,
+                    "minibatch_tokens": tmb, "ms_per_step": round(ms, 4),
+                    "bitwise_equal_to_one_forward": bool(torch.equal(y.view(torch.int16),
+                                                                     ref.view(torch.int16)))})
+        del ring, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def progress(msg: str) -> None:
     """One line on stderr per finished part of the run (the JSON line goes to stdout)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -567,6 +603,8 @@ def main() -> int:
     progress(f"persistent forward timed: {persistent}")
     graph = measure_graph(G, S, args.steps, args.warmup)
     progress(f"graph-replayed forward timed: {graph}")
+    ring = measure_ring(G, S, max(3, args.steps // 4), 1)
+    progress(f"macrobatch ring timed: {ring}")
     library = library_dense_gemms(wl, dev)
     progress(f"library dense GEMMs: {library}")
 
@@ -651,6 +689,7 @@ def main() -> int:
         "library_dense_gemm": library,
         "persistent": persistent,
         "graph": graph,
+        "ring": ring,
         "cpu_baseline": baseline,
         "other_workloads": others,
     }
