@@ -6,6 +6,7 @@
 #include <type_traits>
 
 #include "moe_gemm_plan.h"
+#include "moe_tile_order.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,6 +51,8 @@ struct GemmArgs {
   // large-tile kernel: weight codes K-tiled, [E][N/256][K bytes/128][256][128 bytes] (each stage
   // of a 256-row weight panel is one contiguous 32 KB block), else natural [E][N][K]
   int w_tiled;
+  // large-tile kernel: M groups per band of the work order (big_tile_coords; 0 is taken as 1)
+  int band_gm;
 };
 
 // Epilogue (and grouping) modes of the large-tile kernel.
@@ -113,19 +116,9 @@ __device__ __forceinline__ f32x16_t mfma_mx_sel(int sel, const i32x8_t& a, const
 // 8-lane and 16-lane LDS phases. The swizzle is applied on the global side: the DMA writes a
 // wave's 64 lanes to 1 KB of consecutive LDS, and each lane fetches the chunk for its slot.
 //
-// Work order: the M tiles are cut into bands of about 256 / Nt tiles; all XCDs work on the same
-// band at the same time (so the band's rows and its experts' weights stay in the MALL), and
-// inside a band XCD x takes the x-th eighth of the band's tiles in N-major order, i.e. a block of
-// about Nt/8 weight panels by band-height row panels, about the 32 tiles its CUs run at once and
-// share through its L2. Workgroup L runs on XCD L % 8.
+// Work order: big_tile_coords (moe_tile_order.h), blocks of a band of about 256 tiles per XCD.
 // ------------------------------------------------------------------------------------------------
 constexpr int kBigBN = 256;
-// band height in M tiles: about 256 tiles per band, i.e. about the 32 concurrent workgroups of
-// each XCD per band share
-__host__ __device__ inline int band_rows_for(int Nt) {
-  const int b = (256 + Nt / 2) / Nt;
-  return b < 4 ? 4 : (b > 16 ? 16 : b);
-}
 
 template <int RB>
 __device__ __forceinline__ int big_swz(int row) {
@@ -206,35 +199,6 @@ constexpr int kBigRB = 128;
 // LDS bytes of a large tile's two rings
 __host__ __device__ constexpr int big_lds_bytes(int bm, int rb, int ns, int nsr) {
   return (ns * kBigBN + nsr * bm) * rb;
-}
-
-// The tile of workgroup jx of XCD x over mt_total M tiles and Nt N tiles: the M tiles are cut
-// into bands of band_rows_for(Nt) tiles, all XCDs work on one band at a time, and inside a band
-// XCD x takes the x-th eighth of its tiles in N-major order. False: no tile (surplus workgroup).
-__device__ __forceinline__ bool big_tile_coords(int mt_total, int Nt, int x, int jx, int& ti,
-                                                int& nt) {
-  const int band_m = band_rows_for(Nt);
-  const int nb_full = mt_total / band_m;
-  const int tb_full = band_m * Nt;
-  const int share_full = ((x + 1) * tb_full >> 3) - (x * tb_full >> 3);
-  int band, band_rows, tb;
-  if (jx < nb_full * share_full) {
-    band = jx / share_full;
-    jx -= band * share_full;
-    band_rows = band_m;
-    tb = tb_full;
-  } else {
-    jx -= nb_full * share_full;
-    band = nb_full;
-    band_rows = mt_total - nb_full * band_m;
-    tb = band_rows * Nt;
-    const int share_last = ((x + 1) * tb >> 3) - (x * tb >> 3);
-    if (jx >= share_last) return false;
-  }
-  const int pos = (x * tb >> 3) + jx;
-  nt = pos / band_rows;
-  ti = band * band_m + pos % band_rows;
-  return true;
 }
 
 // One output tile of the large-tile grouped GEMM, M tile ti (an entry of the tile table, or an
@@ -941,7 +905,8 @@ template <int MODE, bool MX, int BM, int RB, int NS, int NSR, bool PIPE = true>
 __device__ __forceinline__ void big_tile(const GemmArgs& p, int x, int jx, uint8_t* lds) {
   const int mt_total = MODE == kEpiWgrad ? p.tiles_total : *p.tile_count;
   int ti, nt;
-  if (!big_tile_coords(mt_total, p.N / kBigBN, x, jx, ti, nt)) return;  // before any barrier
+  // (before any barrier)
+  if (!big_tile_coords(mt_total, p.N / kBigBN, p.band_gm, x, jx, ti, nt)) return;
   big_tile_at<MODE, MX, BM, RB, NS, NSR, PIPE>(p, ti, nt, lds);
 }
 

@@ -530,7 +530,7 @@ hipError_t launch_prepare_weights(const uint16_t* w_gate, const uint16_t* w_up,
 // grid of the large-tile kernel for at most max_mt M tiles and nt N tiles: per XCD at most
 // ceil(tiles / 8) plus one per band, and a multiple of 8 for the XCD remap
 static dim3 big_grid(int max_mt, int nt) {
-  return dim3(8 * ((max_mt * nt + 7) / 8 + max_mt / band_rows_for(nt) + 2));
+  return dim3(8 * big_grid_per_xcd(max_mt, nt));
 }
 
 // the fields of the forward FFN's two GEMMs common to both kernels
@@ -632,6 +632,8 @@ hipError_t launch_expert_ffn(const void* rows, const uint8_t* row_scales, const 
     }
     big_gemm_args(rs, n_src, R, mx, row_src, row_div, a1, a2);
     a1.gu_out = gu_out;
+    a1.band_gm = band_groups_for((2 * m) / kBigBN, bm, R / E_loc);
+    a2.band_gm = band_groups_for(h / kBigBN, bm, R / E_loc);
     if (mx && bm == 192) {  // never with save
       MOE_BIG(kEpiSwiglu, true, 192, g1, a1);
       if (ev) (void)hipEventRecord(ev[1], st);
@@ -747,6 +749,8 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
   b.N = h;
   b.out = dA;
 
+  a.band_gm = band_groups_for(m / kBigBN, kBwdBM, R / E_loc);
+  b.band_gm = band_groups_for(h / kBigBN, kBwdBM, R / E_loc);
   const dim3 ga = big_grid(max_tiles, m / kBigBN), gb = big_grid(max_tiles, h / kBigBN);
   if (mx) MOE_BIG(kEpiDSwiglu, true, kBwdBM, ga, a);
   else MOE_BIG(kEpiDSwiglu, false, kBwdBM, ga, a);

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void forward_persistent_kernel(
         case kPhGemm2:
           need(kPhRank);
           if (ok) {
-            if (!big_tile_coords(ld_relaxed(a.tile_count), a.Nt2, x, j, ti, nt)) ti = -1;
+            if (!big_tile_coords(ld_relaxed(a.tile_count), a.Nt2, 1, x, j, ti, nt)) ti = -1;
             else if (!gemm_step_done(kPhGemm1, a.Nt1)) {
               ok = wait_count(a, a.sync + kSyncTiles + ti, a.Nt1);
               if (ok) acquire();
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void forward_persistent_kernel(
       case kPhGemm1: {
         int ti, nt;
         const int mt = __builtin_amdgcn_readfirstlane(ld_relaxed(a.tile_count));
-        if (!big_tile_coords(mt, a.Nt1, x, j, ti, nt)) {
+        if (!big_tile_coords(mt, a.Nt1, 1, x, j, ti, nt)) {
           counted = false;  // a surplus item
           break;
         }
@@ -499,7 +499,7 @@ hipError_t launch_forward_persistent(const PersistentBuffers& b, int T, int h, i
   a.Nt1 = 2 * m / kBigBN;
   a.Nt2 = h / kBigBN;
   auto per_xcd = [&](int nt) {  // the grouped-GEMM kernels' grid over 8 XCDs
-    return (max_tiles * nt + 7) / 8 + max_tiles / band_rows_for(nt) + 2;
+    return big_grid_per_xcd(max_tiles, nt);
   };
   a.per_xcd[0] = per_xcd(a.Nt1);
   a.per_xcd[1] = per_xcd(a.Nt2);
