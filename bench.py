@@ -107,12 +107,13 @@ def stage_bytes(wl) -> dict:
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = [os.path.join(ROOT, "routing_expert_grouped_amd", "csrc", f)
-                for f in ("moe_gemm_big.h", "moe_gemm_plan.h", "moe_gemm_kernels.hip")]
+                for f in ("moe_gemm_big.h", "moe_gemm_plan.h", "moe_tile_order.h",
+                          "moe_gemm_kernels.hip")]
 
 
 def gemm_source_sha256() -> str:
-    """sha256 of the grouped-GEMM sources (the large-tile device code, its DMA plan and the
-    kernels), concatenated in that order: the key under which GEMM counters are kept."""
+    """sha256 of the grouped-GEMM sources (the large-tile device code, its DMA plan, its work order
+    and the kernels), concatenated in that order: the key under which GEMM counters are kept."""
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
         h.update(open(f, "rb").read())

@@ -240,6 +240,9 @@ moe_status moe_forward(const moe_shape* s, moe_dtype dt, const uint16_t* x,
  * throughput, not correctness. Arguments as moe_forward (no saved state). minibatch_tokens (host,
  * optional) receives the minibatch size. MOE_EINVAL (nothing enqueued) when even one token's
  * minibatch does not fit.
+ * moe_forward_ring_tokens: the largest token count whose forward workspace fits ring_bytes, T if
+ * that is all of them, else rounded down to a multiple of 4 / gcd(k, 4) so that every minibatch's
+ * slice of assign and assign_w stays 16-byte aligned; 0 when no such count fits.
  * ------------------------------------------------------------------------------------------- */
 int32_t moe_forward_ring_tokens(const moe_shape* s, moe_dtype dt, size_t ring_bytes);
 moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,

@@ -639,7 +639,11 @@ int32_t moe_forward_ring_tokens(const moe_shape* s, moe_dtype dt, size_t ring_by
     if (need(mid) <= ring_bytes) lo = mid;
     else hi = mid - 1;
   }
-  return lo;
+  if (lo >= s->T) return s->T;  // one minibatch
+  // every minibatch starts 16-byte aligned in assign / assign_w (k 4-byte entries per token):
+  // a multiple of 4 / gcd(k, 4) tokens
+  const int a = s->k % 4 == 0 ? 1 : (s->k % 2 == 0 ? 2 : 4);
+  return lo / a * a;
 }
 
 moe_status moe_forward_ring(const moe_shape* s, moe_dtype dt, const uint16_t* x,

@@ -229,19 +229,22 @@ def test_forward_ring_minibatch_sizes(lib):
     holds the whole batch; moe_forward_ring refuses a ring that holds no minibatch before any
     launch."""
     L = lib.load()
+    # k = 4: any count keeps assign 16-byte aligned; k = 6 (even): pairs; k = 5 (odd): fours
+    for k, a in ((4, 1), (6, 2), (5, 4)):
+        s = _shape(lib, T=1000, h=512, m=256, E=64, k=k, E_loc=64)
+        full = L.moe_forward_workspace_bytes(ctypes.byref(s), 1)
+        assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, full) == 1000
+        assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, 1 << 40) == 1000
+        prev = 0
+        for frac in (0.05, 0.1, 0.3, 0.5, 0.9):
+            t = L.moe_forward_ring_tokens(ctypes.byref(s), 1, int(full * frac))
+            assert prev <= t < 1000 and t % a == 0 and (t * k * 4) % 16 == 0
+            one = _shape(lib, T=t, h=512, m=256, E=64, k=k, E_loc=64)
+            two = _shape(lib, T=t + a, h=512, m=256, E=64, k=k, E_loc=64)
+            assert L.moe_forward_workspace_bytes(ctypes.byref(one), 1) <= int(full * frac) < \
+                L.moe_forward_workspace_bytes(ctypes.byref(two), 1)
+            prev = t
     s = _shape(lib, T=1000, h=512, m=256, E=64, k=4, E_loc=64)
-    full = L.moe_forward_workspace_bytes(ctypes.byref(s), 1)
-    assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, full) == 1000
-    assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, 1 << 40) == 1000
-    prev = 0
-    for frac in (0.05, 0.1, 0.3, 0.5, 0.9):
-        t = L.moe_forward_ring_tokens(ctypes.byref(s), 1, int(full * frac))
-        assert prev <= t < 1000
-        one = _shape(lib, T=t, h=512, m=256, E=64, k=4, E_loc=64)
-        two = _shape(lib, T=t + 1, h=512, m=256, E=64, k=4, E_loc=64)
-        assert L.moe_forward_workspace_bytes(ctypes.byref(one), 1) <= int(full * frac) < \
-            L.moe_forward_workspace_bytes(ctypes.byref(two), 1)
-        prev = t
     assert L.moe_forward_ring_tokens(ctypes.byref(s), 1, 1000) == 0
     tmb = ctypes.c_int32(-1)
     st = L.moe_forward_ring(ctypes.byref(s), 1, FAKE, FAKE, None, None, None, FAKE, None, FAKE,

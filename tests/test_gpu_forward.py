@@ -1,6 +1,7 @@
 """GPU parity of moe_forward (the whole layer) on scaled-down versions of the five workloads:
 routing and schedule bit-exact, output within tolerance, two runs bitwise identical, and the same
 bits as the separate entry points composed (route, permute, expert FFN, combine)."""
+import math
 import numpy as np
 import pytest
 
@@ -207,11 +208,13 @@ def test_undersized_buffers_are_rejected_before_any_launch():
 
 
 @pytest.mark.parametrize("name,frac", [("tiny", 0.0), ("qwen397", 0.3), ("kimi", 0.45),
-                                       ("glm52", 0.2)])
+                                       ("glm52", 0.2), ("dsv4pro", 0.3)])
 def test_forward_ring_equals_one_forward(name, frac):
     """moe_forward_ring (the tokens streamed through a fixed buffer in minibatches, here a fraction
     of the one-shot workspace: several minibatches and a short last one; frac 0 = a ring that holds
-    a single token) gives bitwise the y of one moe_forward over all tokens."""
+    the smallest minibatch) gives bitwise the y of one moe_forward over all tokens. The DeepSeek-V4-Pro-shaped
+    share (k = 6) takes minibatches of an even token count, where its assignment slices stay
+    16-byte aligned."""
     G = require_gpu()
     base = I.get(name)
     wl = I.scaled(base, **SCALED[name]) if SCALED[name] else base
@@ -226,8 +229,9 @@ def test_forward_ring_equals_one_forward(name, frac):
         sprep = G.moe_prepare_weights(G.make_shape(wl.T, wl.h, wl.m_shared, 1, 1, 1), "bf16",
                                       *shared)
     full = G.moe_forward_workspace_bytes(sh, wl.dtype)
+    a = 4 // math.gcd(wl.k, 4)  # the smallest minibatch: 16-byte aligned assignment slices
     one = G.moe_forward_workspace_bytes(
-        G.make_shape(1, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared), wl.dtype)
+        G.make_shape(a, wl.h, wl.m, wl.E, wl.k, wl.E_loc, wl.m_shared), wl.dtype)
     nbytes = max(one, int(full * frac)) // 256 * 256 + 256
     ring = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     kw = {}
