@@ -69,7 +69,9 @@ typedef struct {
   int32_t m_shared; /* width of a BF16 shared SwiGLU expert over the T tokens, 0 = none */
 } moe_shape;
 
-const char* moe_status_string(moe_status s);
+/* The name and meaning of a status code; any int (a status held in an int, or an unknown code,
+ * which gives "unknown moe_status"). */
+const char* moe_status_string(int code);
 int moe_abi_version(void);
 
 /* Diagnostic: the E4M3 encoder the kernels use (the hardware conversion after a clamp to +-448)

@@ -35,7 +35,7 @@ moe_status check_expert_shape(const moe_shape* s, moe_dtype dt) {
   if (s->m_shared && s->m_shared % 64) return MOE_EUNSUPPORTED;
   // the grouped GEMMs address rows with 32-bit byte offsets
   const size_t el = dt == MOE_MXFP8 ? 1 : 2;
-  if ((size_t)s->T * s->k * (size_t)std::max(s->h, 2 * s->m) * el >= (1ull << 32))
+  if ((size_t)s->T * s->k * std::max((size_t)s->h, 2 * (size_t)s->m) * el >= (1ull << 32))
     return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -49,7 +49,7 @@ moe_status check_backward_shape(const moe_shape* s, moe_dtype dt) {
   const size_t kg = (size_t)wgrad_k_align(dt == MOE_MXFP8);
   const size_t kmax = ((size_t)s->T * s->k + (size_t)s->E_loc * (kg - 1)) / kg * kg;
   if (kmax >= (1ull << 31)) return MOE_EUNSUPPORTED;
-  if ((size_t)std::max(s->h, 2 * s->m) * kmax * el >= (1ull << 32)) return MOE_EUNSUPPORTED;
+  if (std::max((size_t)s->h, 2 * (size_t)s->m) * kmax * el >= (1ull << 32)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -193,8 +193,8 @@ __global__ void shared_offsets_kernel(int32_t* off, int T) {
 
 extern "C" {
 
-const char* moe_status_string(moe_status s) {
-  switch (s) {
+const char* moe_status_string(int code) {
+  switch (code) {
     case MOE_OK: return "MOE_OK";
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape not covered by the kernels";
@@ -249,7 +249,9 @@ moe_status moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_ro
 }
 
 size_t moe_permute_workspace_bytes(const moe_shape* s) {
-  if (!s || s->T < 1 || s->k < 1 || s->E_loc < 1) return 0;
+  if (!s || s->T < 1 || s->k < 1 || s->E_loc < 1 || s->k > kMaxK || s->E_loc > kMaxExperts ||
+      (long long)s->T * s->k > (1ll << 30))
+    return 0;
   return sched_workspace_bytes(s->T * s->k, s->E_loc);
 }
 

@@ -27,6 +27,8 @@ CSRC = os.path.join(ROOT, "routing_expert_grouped_amd", "csrc")
 HEADER = os.path.join(CSRC, "moe_gemm_plan.h")
 KERNELS = os.path.join(CSRC, "moe_gemm_kernels.hip")
 NK_MAX = 200
+# the host replay runs under AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts)
+SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 PROGRAM = r"""
 #include <cstdio>
@@ -79,7 +81,7 @@ def plans():
         src = os.path.join(d, "plan.cpp")
         exe = os.path.join(d, "plan")
         open(src, "w").write(PROGRAM.replace("%NK%", str(NK_MAX)))
-        subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", CSRC, src, "-o", exe],
+        subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", *SAN, "-I", CSRC, src, "-o", exe],
                        check=True)
         out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
     return [json.loads(line) for line in out.splitlines()]

@@ -12,6 +12,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "routing_expert_grouped_amd", "csrc")
+# the host programs run under AddressSanitizer and UndefinedBehaviorSanitizer (any report aborts)
+SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 PROGRAM = r"""
 #include <cstdio>
@@ -70,7 +72,7 @@ def test_every_tile_exactly_once_in_every_grouping():
         exe = os.path.join(d, "order")
         with open(src, "w") as f:
             f.write(PROGRAM)
-        subprocess.run([gxx, "-O2", "-std=c++17", "-I", CSRC, src, "-o", exe], check=True,
+        subprocess.run([gxx, "-O2", "-std=c++17", *SAN, "-I", CSRC, src, "-o", exe], check=True,
                        capture_output=True, timeout=300)
         out = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stdout[-500:]
@@ -102,7 +104,7 @@ def test_band_groups_of_the_workload_shapes():
         exe = os.path.join(d, "g")
         with open(src, "w") as f:
             f.write(prog)
-        subprocess.run([gxx, "-O2", "-std=c++17", "-I", CSRC, src, "-o", exe], check=True,
+        subprocess.run([gxx, "-O2", "-std=c++17", *SAN, "-I", CSRC, src, "-o", exe], check=True,
                        capture_output=True, timeout=300)
         got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
                                               timeout=60).stdout.split()]
