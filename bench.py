@@ -24,6 +24,8 @@ import argparse
 import hashlib
 import json
 import os
+import shutil
+import subprocess
 import sys
 import time
 
@@ -355,6 +357,16 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         plain()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # the same forwards one by one between events on the launch stream: median, min and p90
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        plain()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    step_stats = {"median": round(per_step[steps // 2], 4), "min": round(per_step[0], 4),
+                  "p90": round(per_step[min(steps - 1, (9 * steps) // 10)], 4)}
     t0 = time.perf_counter()
     for ev in events:
         step(ev)
@@ -405,6 +417,7 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
     return {
         "tokens_per_s": round(wl.T / (ms_per_step * 1e-3), 1),
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": step_stats,
         "profiled_ms_per_step": round(profiled_ms, 4),
         "gemm1_tflops": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12, 1),
         "gemm1_mfma_frac": round(fl["gemm1"] / (g1_ms * 1e-3) / 1e12 / peak, 4),
@@ -420,6 +433,22 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         "router_tflops": (round(fl["router"] / (stages["router_logits"] * 1e-3) / 1e12, 1)
                           if fl["router"] and stages["router_logits"] > 0 else None),
     }
+
+
+def gpu_clocks():
+    """The clocks rocm-smi reports for the GPU, read right after the timed forwards (a snapshot:
+    under the grouped GEMMs' load the chip is power-limited and runs below its peak clock), or
+    None when the tool is missing or says nothing parsable."""
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        res = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=30)
+        data = json.loads(res.stdout)
+        card = next(iter(data.values())) if isinstance(data, dict) and data else {}
+        out = {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()}
+        return out or None
+    except Exception:  # no tool, no JSON, no card: the bench runs on without it
+        return None
 
 
 def measure_persistent(G, S: Setup, steps: int, warmup: int):
@@ -599,7 +628,8 @@ def main() -> int:
     S = Setup(G, wl, dev, args.seed)
     progress(f"{wl.name}: inputs and prepared weights ready")
     r = measure_forward(G, S, args.steps, args.warmup, args.flush_steps)
-    progress(f"forward timed: {r['ms_per_step']} ms per step")
+    clocks = gpu_clocks()
+    progress(f"forward timed: {r['ms_per_step']} ms per step (clocks {clocks})")
     persistent = measure_persistent(G, S, args.steps, args.warmup)
     progress(f"persistent forward timed: {persistent}")
     graph = measure_graph(G, S, args.steps, args.warmup)
@@ -682,7 +712,9 @@ def main() -> int:
         "grouped_gemm_mfma_frac": r["grouped_gemm_mfma_frac"],
         "layer_tflops": r["layer_tflops"],
         "router_tflops": r["router_tflops"],
+        "step_ms": r["step_ms"],
         "profiled_ms_per_step": r["profiled_ms_per_step"],
+        "clocks": clocks,
         "stages_ms": r["stages_ms"],
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
