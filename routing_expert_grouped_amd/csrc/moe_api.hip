@@ -554,7 +554,7 @@ moe_status backward_impl(const moe_shape* s, moe_dtype dt, const uint16_t* x, co
   // un-permute below adds the router's part of dx from them
   if (dgate && e == hipSuccess) e = launch_gate_grads(dy, O, inv, w, dgate, dl, T, h, k, hs);
   if (e == hipSuccess) e = launch_kpad_table(offsets, E_loc, wgrad_k_align(mx), koff, hs);
-  if (e == hipSuccess) e = launch_gemm_tiles(offsets, b + L.tiles, R, E_loc, hs);
+  if (e == hipSuccess) e = launch_gemm_tiles(offsets, b + L.tiles, R, E_loc, mx, hs);
   mark(1);
   if (e == hipSuccess)
     e = launch_uncombine(dy, perm, w, offsets, E_loc, b + L.dO, mx ? b + L.dO_s : nullptr, R, h,

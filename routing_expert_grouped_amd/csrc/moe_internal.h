@@ -168,9 +168,10 @@ bool ffn_big(int h, int m);
 // Backward GEMMs (moe_gemm_kernels.hip). Both need h % 256 == 0 and m % 256 == 0.
 // K segments of the weight gradients: each expert's routed rows padded to a multiple of this
 inline int wgrad_k_align(bool mx) { return mx ? 256 : 64; }
-// the M-tile table of the backward's routed-row GEMMs (count + tiles) and its size
+// the M-tile tables of the backward's routed-row GEMMs (count + tiles; dH's 128-row table, then
+// dA's) and their size
 size_t gemm_tiles_bytes(int R, int E_loc);
-hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc,
+hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc, bool mx,
                              hipStream_t st);
 // dG|dU (with the SwiGLU backward) from dO and the prepared W_down rows [e][m][h], then dA from
 // dG|dU and the prepared [W_gate | W_up] rows [e][h][2m]; ev_mid (or null) between the two.
