@@ -211,9 +211,10 @@ def cpu_baseline(wl, inp, weights_of, shared_host, n_tokens: int, min_seconds: f
 def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
     """The expert-path backward of the same layer, timed on its own: one forward that keeps its
     saved state (timed too, as the training forward), then K backward steps from that state, each
-    with HIP events at its stage boundaries. Weight gradients in float32. Then K steps of the whole
-    layer's backward (moe_backward_layer: also the gate-weight, router-matrix and bias gradients
-    and the router's part of dX), timed as a whole."""
+    with HIP events at its stage boundaries, weight gradients in float32 (and, as context, the
+    same steps with bf16 weight gradients). Then K steps of the whole layer's backward
+    (moe_backward_layer: also the gate-weight, router-matrix and bias gradients and the router's
+    part of dX), timed as a whole."""
     import torch
 
     dev = x.device
@@ -249,6 +250,26 @@ def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
             stages[k] += v / args.steps
     for ev in evs + [wev]:
         ev.close()
+    # context for the store-bound weight gradients: the same steps with dW in bf16 (half the
+    # bytes stored); the reported backward keeps float32
+    dw16 = tuple(torch.empty(t.shape, dtype=torch.bfloat16, device=dev) for t in dw)
+    evs16 = [G.HipEvents(G.MOE_BWD_PROFILE_EVENTS, G.BWD_STAGES) for _ in range(args.steps)]
+    for ev in evs16[:1] * args.warmup:
+        G.moe_backward_profiled(sh, wl.dtype, x, dy, saved, pbwd, ev, dx=dx, dw=dw16,
+                                dw_fp32=False, ws=bws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs16:
+        G.moe_backward_profiled(sh, wl.dtype, x, dy, saved, pbwd, ev, dx=dx, dw=dw16,
+                                dw_fp32=False, ws=bws)
+    torch.cuda.synchronize()
+    ms16 = (time.perf_counter() - t0) * 1e3 / args.steps
+    st16 = {k: 0.0 for k in G.BWD_STAGES}
+    for ev in evs16:
+        for k, v in ev.stage_ms().items():
+            st16[k] += v / args.steps
+        ev.close()
+    del dw16
     # the whole layer's backward: the expert path plus the gate-weight and router gradients
     wr = kw.get("w_router")
     lay = lambda: G.moe_backward_layer(sh, wl.dtype, x, dy, saved, pbwd, w_router=wr, dx=dx,
@@ -270,7 +291,10 @@ def time_backward(G, wl, sh, x, wg, wu, wd, prepared, kw, inp, args) -> dict:
             "gemm_mfma_frac": round(flops / (gemm_ms * 1e-3) / 1e12 / peak, 4),
             "flop": flops, "dw_dtype": "f32", "training_forward_ms": round(fwd_saved_ms, 4),
             "layer_backward_ms": round(layer_ms, 4),
-            "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
+            "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+            "bf16_dw": {"ms_per_step": round(ms16, 4),
+                        "wgrad_gate_up": round(st16["wgrad_gate_up"], 4),
+                        "wgrad_down": round(st16["wgrad_down"], 4)}}
 
 
 def expert_roofline(wl, counts, g1_ms: float, g2_ms: float) -> dict:
