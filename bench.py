@@ -24,8 +24,6 @@ import argparse
 import hashlib
 import json
 import os
-import shutil
-import subprocess
 import sys
 import time
 
@@ -459,22 +457,6 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
     }
 
 
-def gpu_clocks():
-    """The clocks rocm-smi reports for the GPU, read right after the timed forwards (a snapshot:
-    under the grouped GEMMs' load the chip is power-limited and runs below its peak clock), or
-    None when the tool is missing or says nothing parsable."""
-    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
-    try:
-        res = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=30)
-        data = json.loads(res.stdout)
-        card = next(iter(data.values())) if isinstance(data, dict) and data else {}
-        out = {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()}
-        return out or None
-    except Exception:  # no tool, no JSON, no card: the bench runs on without it
-        return None
-
-
 def measure_persistent(G, S: Setup, steps: int, warmup: int):
     """The same forward as one persistent kernel (moe_forward_persistent) against the plain
     multi-kernel moe_forward (no stage events), both timed over `steps` back-to-back calls; None
@@ -652,8 +634,7 @@ def main() -> int:
     S = Setup(G, wl, dev, args.seed)
     progress(f"{wl.name}: inputs and prepared weights ready")
     r = measure_forward(G, S, args.steps, args.warmup, args.flush_steps)
-    clocks = gpu_clocks()
-    progress(f"forward timed: {r['ms_per_step']} ms per step (clocks {clocks})")
+    progress(f"forward timed: {r['ms_per_step']} ms per step")
     persistent = measure_persistent(G, S, args.steps, args.warmup)
     progress(f"persistent forward timed: {persistent}")
     graph = measure_graph(G, S, args.steps, args.warmup)
@@ -738,7 +719,6 @@ def main() -> int:
         "router_tflops": r["router_tflops"],
         "step_ms": r["step_ms"],
         "profiled_ms_per_step": r["profiled_ms_per_step"],
-        "clocks": clocks,
         "stages_ms": r["stages_ms"],
         "stages_gbs": r["stages_gbs"],
         "stages_gbs_flushed": r["stages_gbs_flushed"],
