@@ -267,10 +267,14 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
   }
   __syncthreads();
 
-  const int c = tid & 63;
+  // MX: wave w takes columns 32 (w >> 1) .. + 31 and row blocks 2 (w & 1) and 2 (w & 1) + 1, two
+  // lanes per column, so each store instruction writes 32 bytes into each of 32 lines (not 16
+  // bytes into 64) and a wave's column reads hit 64 distinct banks; BF16: column tid & 63
+  const int wv = tid >> 6, ln = tid & 63;
+  const int c = MX ? 32 * (wv >> 1) + (ln >> 1) : ln;
   const size_t col_at = (size_t)kbase * C + (size_t)(c0 + c) * kpad + q0;  // element index
   if constexpr (MX) {
-    const int b = tid >> 6;  // rows 32 b .. 32 b + 31
+    const int b = 2 * (wv & 1) + (ln & 1);  // rows 32 b .. 32 b + 31
     float amax = 0.0f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(tile[32 * b + q][c]));
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     dst_s[(size_t)kbase * C / kMxBlock + ((size_t)(kb >> 3) * C + c0 + c) * 8 + (kb & 7)] =
         (uint8_t)(sx + 127);
   } else {
-    const int b = tid >> 6;  // rows 16 b .. 16 b + 15
+    const int b = wv;  // rows 16 b .. 16 b + 15
     uint32_t pw[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) pw[q] = pack_bf16x2(tile[16 * b + 2 * q][c], tile[16 * b + 2 * q + 1][c]);
