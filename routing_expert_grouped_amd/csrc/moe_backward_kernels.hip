@@ -182,6 +182,9 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
     uint8_t* __restrict__ dst_s) {
   constexpr int RBT = MX ? 128 : 64;
   __shared__ float tile[RBT][65];
+  // rows 64 and up keep their columns XOR 16 (the MX column reads of blocks 64 rows apart would
+  // share banks); the BF16 tile has 64 rows and no skew
+  auto tile_skew = [](int row) { return 16 * ((row >> 6) & 1); };
   const int kk0 = blockIdx.y * RBT;
   if (kk0 >= koff[E_loc]) return;  // uniform: past the last segment
   // the expert whose segment holds kk0 (exactly one: koff[e] <= kk0 < koff[e+1]), found by the
@@ -263,28 +266,29 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[t][cq + j] = v[j];
+    for (int j = 0; j < 8; ++j) tile[t][(cq + j) ^ tile_skew(t)] = v[j];
   }
   __syncthreads();
 
-  // MX: wave w takes columns 32 (w >> 1) .. + 31 and row blocks 2 (w & 1) and 2 (w & 1) + 1, two
-  // lanes per column, so each store instruction writes 32 bytes into each of 32 lines (not 16
-  // bytes into 64) and a wave's column reads hit 64 distinct banks; BF16: column tid & 63
+  // MX: wave w takes columns 16 w .. 16 w + 15, four lanes per column (one per 32-row block), so
+  // each store instruction writes 64 bytes into each of 16 lines; the column skew of rows 64 and
+  // up puts a wave's column reads on 64 distinct banks. BF16: column tid & 63
   const int wv = tid >> 6, ln = tid & 63;
-  const int c = MX ? 32 * (wv >> 1) + (ln >> 1) : ln;
+  const int c = MX ? 16 * wv + (ln >> 2) : ln;
   const size_t col_at = (size_t)kbase * C + (size_t)(c0 + c) * kpad + q0;  // element index
   if constexpr (MX) {
-    const int b = 2 * (wv & 1) + (ln & 1);  // rows 32 b .. 32 b + 31
+    const int b = ln & 3;  // rows 32 b .. 32 b + 31
+    const int cs = c ^ tile_skew(32 * b);  // the column's place in rows 32 b .. 32 b + 31
     float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(tile[32 * b + q][c]));
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(tile[32 * b + q][cs]));
     const int sx = mx_block_exponent(amax);
     const float inv = mx_inv_scale(sx);
     uint32_t cw[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      cw[q] = e4m3_pack4(tile[32 * b + 4 * q][c] * inv, tile[32 * b + 4 * q + 1][c] * inv,
-                         tile[32 * b + 4 * q + 2][c] * inv, tile[32 * b + 4 * q + 3][c] * inv);
+      cw[q] = e4m3_pack4(tile[32 * b + 4 * q][cs] * inv, tile[32 * b + 4 * q + 1][cs] * inv,
+                         tile[32 * b + 4 * q + 2][cs] * inv, tile[32 * b + 4 * q + 3][cs] * inv);
     uint4* d = reinterpret_cast<uint4*>(dst + col_at + 32 * b);
     d[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     d[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
