@@ -680,35 +680,29 @@ hipError_t launch_tile_table(const int32_t* offsets, int E_loc, int bm, int max_
   return hipGetLastError();
 }
 
-// the backward's dH GEMM takes 128-row tiles in both precisions (its SwiGLU-backward epilogue
-// does not fit the register file next to larger accumulators); dA (the store epilogue) takes the
-// forward GEMM-2's 192-row MXFP8 tile when the experts hold 128 rows or more on average
+// the backward's routed-row GEMMs (dH with the SwiGLU-backward epilogue, dA with the store
+// epilogue) take the forward GEMM-2's 192-row MXFP8 tile when the experts hold 128 rows or more on
+// average, else 128-row tiles (BF16 always: its 256-row tile leaves no room for the
+// SwiGLU-backward epilogue beside the accumulators)
 constexpr int kBwdBM = 128;
 
-static int bwd_da_rows(int R, int E_loc, bool mx) {
+static int bwd_tile_rows(int R, int E_loc, bool mx) {
   return (mx && R / E_loc >= 128) ? 192 : kBwdBM;
 }
 
-// one tile table: the count, then (R / 128 + E_loc) entries, room for any tile height >= 128
-static size_t gemm_table_bytes(int R, int E_loc) {
-  return align_up(align_up(sizeof(int)) + (size_t)((R + kBwdBM - 1) / kBwdBM + E_loc) *
-                                              sizeof(int2));
+// the tile table: the count, then room for (R / 128 + E_loc) entries (any tile height >= 128)
+size_t gemm_tiles_bytes(int R, int E_loc) {
+  return align_up(sizeof(int)) + (size_t)((R + kBwdBM - 1) / kBwdBM + E_loc) * sizeof(int2);
 }
 
-size_t gemm_tiles_bytes(int R, int E_loc) { return 2 * gemm_table_bytes(R, E_loc); }
-
-// the tile tables of the backward's routed-row GEMMs: dH's (128 rows) at tiles_ws, dA's after it
 hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc,
                              bool mx, hipStream_t st) {
+  const int bm = bwd_tile_rows(R, E_loc, mx);
+  const int max_tiles = (R + bm - 1) / bm + E_loc;
   uint8_t* tw = reinterpret_cast<uint8_t*>(tiles_ws);
-  const int bms[2] = {kBwdBM, bwd_da_rows(R, E_loc, mx)};
-  for (int t = 0; t < 2; ++t) {
-    uint8_t* tt = tw + t * gemm_table_bytes(R, E_loc);
-    const int max_tiles = (R + bms[t] - 1) / bms[t] + E_loc;
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, E_loc, bms[t],
-                       max_tiles, reinterpret_cast<int2*>(tt + align_up(sizeof(int))),
-                       reinterpret_cast<int*>(tt));
-  }
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, E_loc, bm, max_tiles,
+                     reinterpret_cast<int2*>(tw + align_up(sizeof(int))),
+                     reinterpret_cast<int*>(tw));
   return hipGetLastError();
 }
 
@@ -718,15 +712,11 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
                             float* dgu_f32, uint16_t* dA, const void* tiles_ws, int R, int h,
                             int m, int E_loc, bool mx, hipStream_t st, hipEvent_t ev_mid) {
   if (!ffn_big(h, m) || m % kBigBN) return hipErrorInvalidValue;
-  const int max_tiles = (R + kBwdBM - 1) / kBwdBM + E_loc;
+  const int bm = bwd_tile_rows(R, E_loc, mx);
+  const int max_tiles = (R + bm - 1) / bm + E_loc;
   const uint8_t* tw = reinterpret_cast<const uint8_t*>(tiles_ws);
   const int* tile_count = reinterpret_cast<const int*>(tw);
   const int2* tiles = reinterpret_cast<const int2*>(tw + align_up(sizeof(int)));
-  const int bm_da = bwd_da_rows(R, E_loc, mx);
-  const int max_tiles_da = (R + bm_da - 1) / bm_da + E_loc;
-  const uint8_t* tw_da = tw + gemm_table_bytes(R, E_loc);
-  const int* tile_count_da = reinterpret_cast<const int*>(tw_da);
-  const int2* tiles_da = reinterpret_cast<const int2*>(tw_da + align_up(sizeof(int)));
   const size_t el = mx ? 1 : 2;
 
   // dH = dO W_down^T (K = h, N = m) with the SwiGLU backward in the epilogue -> dG | dU
@@ -761,19 +751,20 @@ hipError_t launch_bwd_dgrad(const void* dO, const uint8_t* dO_s, const int32_t* 
   b.w_stride = (size_t)h * 2 * m * el;
   b.ws_stride = (size_t)h * (2 * m / kMxBlock);
   b.offsets = offsets;
-  b.tiles = tiles_da;
-  b.tile_count = tile_count_da;
+  b.tiles = tiles;
+  b.tile_count = tile_count;
   b.K = 2 * m;
   b.N = h;
   b.out = dA;
 
-  a.band_gm = band_groups_for(m / kBigBN, kBwdBM, R / E_loc);
-  b.band_gm = band_groups_for(h / kBigBN, bm_da, R / E_loc);
-  const dim3 ga = big_grid(max_tiles, m / kBigBN), gb = big_grid(max_tiles_da, h / kBigBN);
-  if (mx) MOE_BIG(kEpiDSwiglu, true, kBwdBM, ga, a);
+  a.band_gm = band_groups_for(m / kBigBN, bm, R / E_loc);
+  b.band_gm = band_groups_for(h / kBigBN, bm, R / E_loc);
+  const dim3 ga = big_grid(max_tiles, m / kBigBN), gb = big_grid(max_tiles, h / kBigBN);
+  if (mx && bm == 192) MOE_BIG(kEpiDSwiglu, true, 192, ga, a);
+  else if (mx) MOE_BIG(kEpiDSwiglu, true, kBwdBM, ga, a);
   else MOE_BIG(kEpiDSwiglu, false, kBwdBM, ga, a);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
-  if (mx && bm_da == 192) MOE_BIG(kEpiStore, true, 192, gb, b);
+  if (mx && bm == 192) MOE_BIG(kEpiStore, true, 192, gb, b);
   else if (mx) MOE_BIG(kEpiStore, true, kBwdBM, gb, b);
   else MOE_BIG(kEpiStore, false, kBwdBM, gb, b);
   return hipGetLastError();

@@ -168,8 +168,7 @@ bool ffn_big(int h, int m);
 // Backward GEMMs (moe_gemm_kernels.hip). Both need h % 256 == 0 and m % 256 == 0.
 // K segments of the weight gradients: each expert's routed rows padded to a multiple of this
 inline int wgrad_k_align(bool mx) { return mx ? 256 : 64; }
-// the M-tile tables of the backward's routed-row GEMMs (count + tiles; dH's 128-row table, then
-// dA's) and their size
+// the M-tile table of the backward's routed-row GEMMs (count + tiles) and its size
 size_t gemm_tiles_bytes(int R, int E_loc);
 hipError_t launch_gemm_tiles(const int32_t* offsets, void* tiles_ws, int R, int E_loc, bool mx,
                              hipStream_t st);
