@@ -617,7 +617,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this build has no multi-GPU path; see DESIGN.md for how it would shard.",
+              "the library runs one GPU's share of the layer and has no multi-GPU path.",
               file=sys.stderr)
         return 2
 
