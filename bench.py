@@ -50,6 +50,9 @@ def parse():
                     help="repeat the oracle's sample until this much wall time has run")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward timing of workloads that define one")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the macrobatch-ring timing (its minibatch forwards run the same GEMM "
+                         "kernels on fewer rows, which would mix into per-kernel profiles)")
     ap.add_argument("--others", default="tiny,dsv4pro,qwen397,kimi",
                     help="further workloads measured as extra keys ('' for none)")
     ap.add_argument("--other-steps", type=int, default=10)
@@ -639,7 +642,7 @@ def main() -> int:
     progress(f"persistent forward timed: {persistent}")
     graph = measure_graph(G, S, args.steps, args.warmup)
     progress(f"graph-replayed forward timed: {graph}")
-    ring = measure_ring(G, S, max(3, args.steps // 4), 1)
+    ring = None if args.no_ring else measure_ring(G, S, max(3, args.steps // 4), 1)
     progress(f"macrobatch ring timed: {ring}")
     library = library_dense_gemms(wl, dev)
     progress(f"library dense GEMMs: {library}")

@@ -11,7 +11,7 @@
 // of Nt * gm / 8 weight panels by band / gm row panels: the ~32 tiles its CUs run at once, which
 // share their operands through the XCD's L2. A routed-row tile is then fetched into an XCD's L2
 // by 8 / gm XCDs per band, an expert's weight panel by as many XCDs as M groups hold one of its
-// tiles; band_groups_for picks gm to balance the two. gm = 1 is a plain N-major order.
+// tiles; band_groups_for picks gm. gm = 1 is a plain N-major order.
 #pragma once
 
 #if defined(__HIPCC__) || defined(__HIP__)
@@ -28,17 +28,15 @@ MOE_TO_HD inline int band_rows_for(int Nt) {
   return b < 4 ? 4 : (b > 16 ? 16 : b);
 }
 
-// M groups per band (1, 2 or 4) for Nt N tiles of bm-row M tiles over experts of about
-// rows_per_expert rows. With experts that span a band, XCD blocks of (8 / gm) x gm fetch
-// (8 / gm) * band * bm row lines and gm * Nt * 256 weight lines per K byte, which balance at
-// gm = sqrt(8 * band * bm / (Nt * 256)) (rounded to a power of two); experts of at most two tiles
-// read each weight panel once whatever the grouping, so there the next larger gm is taken.
+// M groups per band for Nt N tiles of bm-row M tiles over experts of about rows_per_expert rows.
+// Experts of at most two tiles share a weight panel between at most two M tiles, so the grouping
+// mostly decides how many XCDs fetch each routed-row tile: 4 M groups (2 N groups). Larger experts
+// share their weight panels between the M tiles of a band, and a band's N-major order keeps those
+// tiles on one XCD: 1 (measured: 4 M groups cut the GLM-5.2-shaped GEMM-1's fabric traffic by 16%, 2 raised the
+// DeepSeek-V4-Pro-shaped share's by 15%; the kernel times did not move).
 MOE_TO_HD inline int band_groups_for(int Nt, int bm, long long rows_per_expert) {
-  const long long v = 8LL * band_rows_for(Nt) * bm;  // compared with Nt * 256 * gm^2
-  const long long u = (long long)Nt * 256;
-  int gm = v >= 8 * u ? 4 : (v >= 2 * u ? 2 : 1);
-  if (rows_per_expert <= 2LL * bm && gm < 4) gm *= 2;
-  return gm;
+  (void)Nt;
+  return rows_per_expert <= 2LL * bm ? 4 : 1;
 }
 
 // workgroups per XCD that a launch over at most max_mt M tiles and Nt N tiles needs: every

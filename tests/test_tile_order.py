@@ -80,20 +80,22 @@ def test_every_tile_exactly_once_in_every_grouping():
 
 
 def test_band_groups_of_the_workload_shapes():
-    """The grouping each launch of the five workload shapes takes (tile rows, N tiles and mean
-    routed rows per expert as the launchers pass them), against the choice a per-band count of the
-    rows and weight panels each XCD fetches favours for those shapes."""
+    """The grouping each launch of the workload shapes takes (tile rows, N tiles and mean routed
+    rows per expert as the launchers pass them): four M groups where the experts hold at most two
+    tiles (their weight panels are fetched once either way), the plain N-major order otherwise."""
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("g++ not available")
     cases = [  # (N tiles, tile rows, rows per expert, expected M groups)
         (16, 192, 256, 4),    # GLM-5.2-shaped GEMM-1 (MXFP8, 256 experts, top-8 of 8192 tokens)
         (24, 192, 256, 4),    # its GEMM-2
-        (16, 192, 2730, 2),   # Kimi-shaped share GEMM-1 (6 local experts)
+        (16, 192, 2730, 1),   # Kimi-shaped share GEMM-1 (6 local experts)
         (28, 192, 2730, 1),   # its GEMM-2
-        (24, 256, 2048, 2),   # DeepSeek-V4-Pro-shaped share GEMM-1 (BF16)
+        (24, 256, 2048, 1),   # DeepSeek-V4-Pro-shaped share GEMM-1 (BF16)
         (8, 128, 80, 4),      # Qwen-shaped GEMM-1 (512 experts, top-10 of 4096 tokens)
         (16, 128, 80, 4),     # its GEMM-2
+        (8, 192, 384, 4),     # two tiles per expert: still four M groups
+        (8, 192, 385, 1),     # just over two tiles
     ]
     prog = '#include <cstdio>\n#include "moe_tile_order.h"\nint main() {\n'
     for nt, bm, rpe, _ in cases:
