@@ -33,6 +33,7 @@ import moe_inputs as I_
 
 METRIC = "MoE layer fwd tokens/s on 1 GPU + grouped-GEMM % MFMA peak (BF16/MXFP8)"
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}  # MI355X dense matrix peaks
+PEAK_FP32_MFMA_TFLOPS = 157.3  # the router's float32 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 
 
@@ -439,7 +440,7 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         ms = st[name]
         return round(by[name] / (ms * 1e-3) / 1e9, 1) if ms > 0 and by[name] else None
 
-    return {
+    r = {
         "tokens_per_s": round(wl.T / (ms_per_step * 1e-3), 1),
         "ms_per_step": round(ms_per_step, 4),
         "step_ms": step_stats,
@@ -458,6 +459,9 @@ def measure_forward(G, S: Setup, steps: int, warmup: int, flush_steps: int) -> d
         "router_tflops": (round(fl["router"] / (stages["router_logits"] * 1e-3) / 1e12, 1)
                           if fl["router"] and stages["router_logits"] > 0 else None),
     }
+    r["router_fp32_mfma_frac"] = (round(r["router_tflops"] / PEAK_FP32_MFMA_TFLOPS, 4)
+                                  if r["router_tflops"] else None)
+    return r
 
 
 def measure_persistent(G, S: Setup, steps: int, warmup: int):
@@ -720,6 +724,7 @@ def main() -> int:
         "grouped_gemm_mfma_frac": r["grouped_gemm_mfma_frac"],
         "layer_tflops": r["layer_tflops"],
         "router_tflops": r["router_tflops"],
+        "router_fp32_mfma_frac": r["router_fp32_mfma_frac"],
         "step_ms": r["step_ms"],
         "profiled_ms_per_step": r["profiled_ms_per_step"],
         "stages_ms": r["stages_ms"],

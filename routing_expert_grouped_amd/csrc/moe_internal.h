@@ -119,9 +119,9 @@ inline bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
 // ------------------------------------------------------------------------------------------------
 // Host-side launchers (each returns hipGetLastError() after enqueueing)
 // ------------------------------------------------------------------------------------------------
-// Router (moe_route_kernels.hip): the logits from x (staged through LDS) and the router matrix
-// converted once to float32 and interleaved by 8 columns, in router_xf_bytes(T, h, E) bytes of
-// scratch
+// Router (moe_route_kernels.hip): the logits on the matrix cores from x and the router matrix
+// interleaved by 8 columns (bf16), in router_xf_bytes(T, h, E) bytes of scratch (the size of the
+// float32 interleaved copy the persistent forward's vector-ALU router reads)
 size_t router_xf_bytes(int T, int h, int E);
 hipError_t launch_router_logits_xf(const uint16_t* x, const uint16_t* w_router, const float* bias,
                                    float* logits, int T, int h, int E, float* scratch,
