@@ -751,14 +751,27 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
     }
     lds_barrier();
     const int c16 = tid & 31;  // 16-byte chunk of the row: output columns n0 + 8 c16 .. + 8
+    // rows rr0 + tid / 32, eight rows per pass; a group's LDS reads all go out before its stores
+    // (left alone, the compiler moves each read into its row's store condition and waits for it
+    // there, one LDS latency per row)
+    constexpr int NPASS = BM / 8, GRP = 8;
+    static_assert(NPASS % GRP == 0, "whole groups of passes");
 #pragma unroll
-    for (int rr0 = 0; rr0 < BM; rr0 += 8) {
-      const int rr = rr0 + (tid >> 5);
-      const int r = row0 + rr;
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + rr * RS + 16 * c16);
-      if (r < row_end)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)r * p.N + n0 +
-                                  8 * c16) = v;
+    for (int q0 = 0; q0 < NPASS; q0 += GRP) {
+      uint4 v[GRP];
+#pragma unroll
+      for (int q = 0; q < GRP; ++q)
+        v[q] = *reinterpret_cast<const uint4*>(lds + (8 * (q0 + q) + (tid >> 5)) * RS + 16 * c16);
+#pragma unroll
+      for (int q = 0; q < GRP; ++q)  // (after all of the group's reads: one wait for them)
+        asm volatile("" : "+v"(v[q].x), "+v"(v[q].y), "+v"(v[q].z), "+v"(v[q].w));
+#pragma unroll
+      for (int q = 0; q < GRP; ++q) {
+        const int r = row0 + 8 * (q0 + q) + (tid >> 5);
+        if (r < row_end)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)r * p.N + n0 +
+                                    8 * c16) = v[q];
+      }
     }
   } else if constexpr (MODE == kEpiDSwiglu) {
     // N = m dH columns. The 32-column tile i starting at column nb is one block of dG and one of
@@ -882,18 +895,27 @@ __device__ __forceinline__ void big_tile_at(const GemmArgs& p, int ti, int nt, u
         o = hc ? p.out2 : p.out;
         col = (n0 >> 1) + 4 * j4;
       }
+      // rows rr0 + tid / 64, four per pass: every pass's LDS read goes out before the stores (one
+      // LDS latency per half instead of one per row), and the output type is chosen once
+      constexpr int NPASS = BM / 8;
+      f32x4_t v[NPASS];
 #pragma unroll
-      for (int rr0 = 0; rr0 < BM / 2; rr0 += 4) {
-        const int rr = rr0 + (tid >> 6);
-        const int r = row0 + (BM / 2) * half + rr;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(lds + rr * RSW + 4 * lcol);
-        const size_t at = ebase + (size_t)r * ld + col;
-        if (p.out_f32) {
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(o) + at) = v;
-        } else {
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + at) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
+      for (int q = 0; q < NPASS; ++q)
+        v[q] = *reinterpret_cast<const f32x4_t*>(lds + (4 * q + (tid >> 6)) * RSW + 4 * lcol);
+#pragma unroll
+      for (int q = 0; q < NPASS; ++q)  // (after all the reads: one wait for them)
+        asm volatile("" : "+v"(v[q][0]), "+v"(v[q][1]), "+v"(v[q][2]), "+v"(v[q][3]));
+      const size_t at0 = ebase + (size_t)(row0 + (BM / 2) * half + (tid >> 6)) * ld + col;
+      if (p.out_f32) {
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q)
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(o) + at0 + (size_t)(4 * q) * ld) =
+              v[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q)
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + at0 + (size_t)(4 * q) * ld) =
+              make_uint2(pack_bf16x2(v[q][0], v[q][1]), pack_bf16x2(v[q][2], v[q][3]));
       }
     }
   }
