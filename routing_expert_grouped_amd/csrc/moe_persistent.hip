@@ -38,7 +38,7 @@ namespace moe {
 namespace {
 
 enum Phase : int {
-  kPhWi = 0,   // router matrix as float32, interleaved (router layers)
+  kPhWi = 0,   // router matrix as bf16, interleaved by 8 columns (router layers)
   kPhQuant,    // MXFP8: each token quantised once (GEMM-1 gathers its rows from these)
   kPhLogits,   // router logits
   kPhTopk,     // top-k and gate weights
@@ -57,7 +57,7 @@ enum Phase : int {
 // combine three vectors' rows at once.
 constexpr int kWiSteps = 16;        // 8-column steps of the router matrix per item
 constexpr int kQuantJ = 4;          // quantisation blocks per thread per item
-constexpr int kLogitTokens = 16;    // tokens per router item
+constexpr int kLogitTokens = kRouterTileTokens;  // tokens per router item (one router tile)
 constexpr int kTopkTokens = 16;     // tokens per top-k item (4 per wave)
 constexpr int kCombineTokens = 4;   // tokens per combine item
 
@@ -77,7 +77,7 @@ struct PersistArgs {
   const int32_t* assign;  // the assignments the schedule reads: given, or the top-k output
   const float* gate_w;    // their gate weights
   uint16_t* y;
-  float* wi;
+  float* wi;  // the interleaved router matrix (bf16 in a float32-sized scratch)
   float* logits;
   int32_t* idx;
   float* tw;
@@ -210,8 +210,7 @@ __global__ __launch_bounds__(256, 1) void forward_persistent_kernel(
   constexpr int BM = kPersistentRows;
   constexpr int NS = big_ns(MX, BM), NSR = big_nsr(MX, BM);
   constexpr int LDS = big_lds_bytes(BM, kBigRB, NS, NSR);
-  static_assert(LDS >= router_lds_floats(kLogitTokens) * 4 && LDS >= 4 * 1024 * 4,
-                "LDS of the other steps");
+  static_assert(LDS >= 4 * 1024 * 4, "LDS of the other steps");
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
   // four control words (ticket, ok, M tile, N tile) at the end of the LDS: written by thread 0
   // between items, read by every thread before the barrier that starts the item
@@ -357,7 +356,8 @@ __global__ __launch_bounds__(256, 1) void forward_persistent_kernel(
         const int nvb = (a.h / 8 + kWiSteps - 1) / kWiSteps;
         const int eb = j / nvb, v0 = (j % nvb) * kWiSteps;
         for (int v = v0; v < v0 + kWiSteps && v < a.h / 8; ++v)
-          w_interleave_one(a.w_router, a.E, a.h, a.wi, eb * 256 + tid, v);
+          w_interleave_bf16_one(a.w_router, a.E, a.h, reinterpret_cast<uint16_t*>(a.wi),
+                                eb * 256 + tid, v);
         break;
       }
       case kPhQuant:
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256, 1) void forward_persistent_kernel(
         break;
       case kPhLogits: {
         const int nbx = (a.T + kLogitTokens - 1) / kLogitTokens;
-        router_logits_tile<kLogitTokens>(a.x, a.wi, a.bias, a.logits, a.T, a.h, a.E, j % nbx,
-                                         j / nbx, reinterpret_cast<float*>(lds));
+        router_logits_mfma_tile(a.x, reinterpret_cast<const uint16_t*>(a.wi), a.bias, a.logits,
+                                a.T, a.h, a.E, j % nbx, j / nbx);
         break;
       }
       case kPhTopk:
